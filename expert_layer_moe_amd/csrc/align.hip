@@ -1,0 +1,156 @@
+// Expert align: a stable counting sort of the (token, slot) assignments by
+// expert, each expert segment padded to the GEMM block M.
+//
+// Block granularity per expert follows the combine bookkeeping of "[SGLang]
+// Single Batch Overlap for MoE models" (combine signal section: one signal per
+// expert and 64-token block); padding rows of the gathered batch ("DP
+// Attention and TBO for DeepSeek-V4 on MI355X", PrefillDelayer section) carry
+// no assignment and are skipped.
+//
+// One 1024-thread workgroup: LDS histogram -> wave scan of the padded counts
+// -> stable scatter in 1024-assignment chunks.  Inside a chunk, a lane's rank
+// among the lanes of its wave with the same expert comes from nine ballots
+// over the bits of the expert id; ranks across the chunk's 16 waves come from
+// per-wave counts in LDS.  The result is unique and deterministic.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / kWave;
+constexpr int kMaxSeg = 257;  // 256 routed experts + 1 shared
+
+// Expert of assignment a in the virtual [T, k + n_shared] slot grid, or -1.
+// Slot k (when n_shared) is the shared expert E of every valid row (a row is
+// valid iff its first routed id is valid).
+__device__ __forceinline__ int seg_of(const int32_t* ids, int a, int k, int kk,
+                                      int E) {
+  const int t = a / kk, j = a - t * kk;
+  if (j < k) {
+    const int e = ids[(size_t)t * k + j];
+    return (e >= 0 && e < E) ? e : -1;
+  }
+  const int e0 = ids[(size_t)t * k];
+  return (e0 >= 0 && e0 < E) ? E : -1;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int ns, int bm,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
+    int32_t* __restrict__ slot_pos) {
+  __shared__ int cnt[kMaxSeg];
+  __shared__ int base[kMaxSeg];
+  __shared__ int wcnt[kAlignWaves][kMaxSeg];
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int nseg = E + ns;
+  const int kk = k + ns;
+  const int n_assign = T * kk;
+
+  for (int i = tid; i < kMaxSeg; i += kAlignThreads) cnt[i] = 0;
+  for (int i = tid; i < kAlignWaves * kMaxSeg; i += kAlignThreads)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+
+  for (int a = tid; a < n_assign; a += kAlignThreads) {
+    const int e = seg_of(ids, a, k, kk, E);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // Exclusive scan of the padded counts by wave 0 (5 segments per lane).
+  if (wave == 0) {
+    int local[5];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int seg = lane * 5 + q;
+      const int c = seg < nseg ? cnt[seg] : 0;
+      local[q] = (c + bm - 1) / bm * bm;
+      sum += local[q];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int seg = lane * 5 + q;
+      if (seg < nseg) {
+        base[seg] = run;
+        offsets[seg] = run;
+      }
+      run += local[q];
+    }
+    if (lane == kWave - 1) {
+      offsets[nseg] = inc;
+      *n_post = inc;
+    }
+  }
+  __syncthreads();
+
+  // Sentinels at the tail of each segment, and the expert of each block.
+  for (int seg = tid; seg < nseg; seg += kAlignThreads) {
+    const int c = cnt[seg];
+    const int p = (c + bm - 1) / bm * bm;
+    const int o = base[seg];
+    for (int i = c; i < p; ++i) sorted_ids[o + i] = -1;
+    for (int b = 0; b < p / bm; ++b) block_expert[o / bm + b] = seg;
+  }
+
+  // Stable scatter, chunk by chunk in flat assignment order.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int chunk = 0; chunk < n_assign; chunk += kAlignThreads) {
+    const int a = chunk + tid;
+    const int e = a < n_assign ? seg_of(ids, a, k, kk, E) : -1;
+    const unsigned key = static_cast<unsigned>(e + 1);  // 0..257: 9 bits
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (key >> b) & 1u;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(same & lt_mask);
+    if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (e >= 0) {
+      int pre = 0;
+      for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
+      const int pos = base[e] + pre + rank;
+      const int t = a / kk, j = a - t * kk;
+      sorted_ids[pos] = t * k + (j < k ? j : 0);
+      if (slot_pos) slot_pos[a] = pos;
+    }
+    __syncthreads();
+    for (int seg = tid; seg < nseg; seg += kAlignThreads) {
+      int s = 0;
+      for (int w = 0; w < kAlignWaves; ++w) {
+        s += wcnt[w][seg];
+        wcnt[w][seg] = 0;
+      }
+      base[seg] += s;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
+                        int bm, int32_t* sorted_ids, int32_t* block_expert,
+                        int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
+                     E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
+                     slot_pos);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,286 @@
+// C ABI of the MoE layer: validation, workspace layout, launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+constexpr int kMaxE = 256;
+constexpr int kMaxTopk = 16;
+constexpr int kDefaultBM = 32;
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout of one moe_forward call.
+struct Plan {
+  int T, H, E, ns, I, k;
+  int act, w;
+  int bm, ks;
+  int cap;  // capacity of the sorted row list (multiple of bm)
+  size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
+      off_slot, off_h, off_y, total;
+};
+
+int check_desc(const moe_desc* d, int32_t topk) {
+  if (d == nullptr) return MOE_ERR_INVALID_ARG;
+  if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->E > kMaxE)
+    return MOE_ERR_INVALID_ARG;
+  if (d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
+  if (topk < 1 || topk > d->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
+  if (d->block_m != 0 && d->block_m != kDefaultBM) return MOE_ERR_UNSUPPORTED;
+  const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32;
+  const bool bf16 = d->act_dtype == MOE_BF16 && d->w_dtype == MOE_BF16;
+  const bool fp8 = d->act_dtype == MOE_BF16 && d->w_dtype == MOE_FP8_E4M3;
+  if (!f32 && !bf16 && !fp8) return MOE_ERR_UNSUPPORTED;
+  if (d->H % 64 != 0 || d->I % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (fp8) {
+    if (d->H % 128 != 0 || d->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    if (d->w13_scale == nullptr || d->w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
+  }
+  // sizes must fit the kernels' 32-bit row/element indexing of the row list
+  const long long rows = (long long)d->T * (topk + d->n_shared) +
+                         (long long)(d->E + d->n_shared) * kDefaultBM;
+  if (rows > (1LL << 30) || (long long)d->T * d->H > (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int choose_ks(const moe_desc* d) {
+  if (d->act_dtype != MOE_BF16) return 1;
+  const int ksteps = d->H / 32;
+  const long long base = (long long)((d->T + 15) / 16) * ((d->E + 63) / 64);
+  int ks = 1;
+  while (base * ks < 512 && ksteps % (ks * 2) == 0) ks *= 2;
+  return ks;
+}
+
+int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
+  const int st = check_desc(d, topk);
+  if (st != MOE_OK) return st;
+  p->T = d->T; p->H = d->H; p->E = d->E; p->ns = d->n_shared; p->I = d->I;
+  p->k = topk; p->act = d->act_dtype; p->w = d->w_dtype;
+  p->bm = kDefaultBM;
+  p->ks = choose_ks(d);
+  const size_t kk = (size_t)topk + p->ns;
+  p->cap = (int)round_up((size_t)p->T * kk + (size_t)(p->E + p->ns) * (p->bm - 1), p->bm);
+  const size_t act_h = (p->act == MOE_F32) ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = round_up(o + bytes, kAlign); return r; };
+  p->off_part = take((size_t)p->ks * p->T * p->E * 4);
+  p->off_ids = take((size_t)p->T * topk * 4);
+  p->off_w = take((size_t)p->T * topk * 4);
+  p->off_sorted = take((size_t)p->cap * 4);
+  p->off_bexp = take((size_t)(p->cap / p->bm) * 4);
+  p->off_offs = take((size_t)(p->E + p->ns + 1) * 4);
+  p->off_npost = take(4);
+  p->off_slot = take((size_t)p->T * kk * 4);
+  p->off_h = take((size_t)p->cap * p->I * act_h);
+  p->off_y = take((size_t)p->cap * p->H * 4);
+  p->total = o;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---- measurement hooks -------------------------------------------------------
+enum Stage { S_LOGITS = 0, S_TOPK, S_ALIGN, S_GATE_UP, S_DOWN, S_COMBINE, S_COUNT };
+const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align",
+                                    "gate_up", "down", "combine"};
+
+struct ProfRecord {
+  int stage;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+
+struct StageTimer {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  StageTimer(int st, hipStream_t str) : stage(st), s(str) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      a = b = nullptr;
+      return;
+    }
+    (void)hipEventRecord(a, s);
+  }
+  ~StageTimer() {
+    if (a == nullptr) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({stage, a, b});
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_desc* desc, int32_t topk) {
+  Plan p;
+  if (make_plan(desc, topk, &p) != MOE_OK) return 0;
+  return p.total;
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dtype combination or shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+              const void* router_w, int32_t topk, int32_t* topk_ids,
+              float* topk_w, float* logits, void* workspace,
+              size_t workspace_bytes, moe_stream_t stream) {
+  Plan p;
+  const int st = make_plan(desc, topk, &p);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !topk_ids || !topk_w || !workspace) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* part = at<float>(workspace, p.off_part);
+  if (moe::launch_route_logits(p.act == MOE_BF16, x, valid_rows, router_w, part,
+                               p.T, p.H, p.E, p.ks, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (moe::launch_route_topk(part, p.ks, valid_rows, p.T, p.E, p.k, topk_ids,
+                             topk_w, logits, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
+              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+              int32_t* expert_offsets, int32_t* n_post_padded,
+              moe_stream_t stream) {
+  if (desc == nullptr) return MOE_ERR_INVALID_ARG;
+  if (desc->T < 1 || desc->E < 1 || desc->E > kMaxE) return MOE_ERR_INVALID_ARG;
+  if (topk < 1 || topk > desc->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
+  if (block_m < 1 || block_m > 256) return MOE_ERR_INVALID_ARG;
+  if (!topk_ids || !sorted_ids || !block_expert || !expert_offsets || !n_post_padded)
+    return MOE_ERR_INVALID_ARG;
+  if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+  if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
+                        block_expert, expert_offsets, n_post_padded, nullptr,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                const void* router_w, const void* w13, const void* w2,
+                int32_t topk, void* out, void* workspace,
+                size_t workspace_bytes, moe_stream_t stream) {
+  Plan p;
+  const int st = make_plan(desc, topk, &p);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !w13 || !w2 || !out || !workspace) return MOE_ERR_INVALID_ARG;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  float* part = at<float>(ws, p.off_part);
+  int32_t* ids = at<int32_t>(ws, p.off_ids);
+  float* wts = at<float>(ws, p.off_w);
+  int32_t* sorted = at<int32_t>(ws, p.off_sorted);
+  int32_t* bexp = at<int32_t>(ws, p.off_bexp);
+  int32_t* offs = at<int32_t>(ws, p.off_offs);
+  int32_t* npost = at<int32_t>(ws, p.off_npost);
+  int32_t* slot = at<int32_t>(ws, p.off_slot);
+  void* h = at<void>(ws, p.off_h);
+  float* y = at<float>(ws, p.off_y);
+  const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
+
+  {
+    StageTimer tm(S_LOGITS, s);
+    if (moe::launch_route_logits(p.act == MOE_BF16, x, valid_rows, router_w, part,
+                                 p.T, p.H, p.E, p.ks, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_TOPK, s);
+    if (moe::launch_route_topk(part, p.ks, valid_rows, p.T, p.E, p.k, ids, wts,
+                               nullptr, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_ALIGN, s);
+    if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
+                          slot, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_GATE_UP, s);
+    if (moe::launch_gate_up(wkind, x, w13, desc->w13_scale, sorted, bexp, npost, h,
+                            p.H, p.I, p.k, p.bm, p.cap, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_DOWN, s);
+    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, y, p.H, p.I, p.bm,
+                         p.cap, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_COMBINE, s);
+    if (moe::launch_combine(y, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+                            p.act == MOE_BF16, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+int moe_num_stages(void) { return S_COUNT; }
+
+const char* moe_stage_name(int stage) {
+  return (stage >= 0 && stage < S_COUNT) ? kStageNames[stage] : "";
+}
+
+int moe_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = enable != 0;
+  return MOE_OK;
+}
+
+int moe_profile_read(double* stage_ms, int32_t* stage_launches, int32_t n) {
+  if (stage_ms == nullptr || stage_launches == nullptr || n < 0) return MOE_ERR_INVALID_ARG;
+  std::vector<ProfRecord> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    recs.swap(g_prof);
+  }
+  for (int i = 0; i < n; ++i) {
+    stage_ms[i] = 0.0;
+    stage_launches[i] = 0;
+  }
+  int status = MOE_OK;
+  for (const ProfRecord& r : recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      status = MOE_ERR_HIP;
+    else if (r.stage < n) {
+      stage_ms[r.stage] += ms;
+      stage_launches[r.stage] += 1;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  return status;
+}
+
+}  // extern "C"

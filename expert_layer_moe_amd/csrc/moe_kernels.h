@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (internal to libmoe_amd).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- route -----------------------------------------------------------------
+// Partial router logits: part[z][t][e] = sum over the z-th K chunk of
+// x[t,:] * R[e,:].  bf16 inputs use MFMA; fp32 inputs use a plain FMA loop
+// (ks must be 1 then).  Rows with valid == 0 are not read and get 0.
+hipError_t launch_route_logits(bool bf16, const void* x, const uint8_t* valid,
+                               const void* R, float* part, int T, int H, int E,
+                               int ks, hipStream_t s);
+// Sum the ks partials (fixed order), pick top-k, softmax over the picks.
+hipError_t launch_route_topk(const float* part, int ks, const uint8_t* valid,
+                             int T, int E, int k, int32_t* ids, float* w,
+                             float* logits_out, hipStream_t s);
+
+// ---- align -----------------------------------------------------------------
+// Stable counting sort of assignments by expert (n_shared extra always-on
+// segments of every valid row when n_shared > 0).  slot_pos may be null.
+hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
+                        int bm, int32_t* sorted_ids, int32_t* block_expert,
+                        int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
+                        hipStream_t s);
+
+// ---- expert GEMMs ------------------------------------------------------------
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+// h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r.
+hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
+                          const float* s13, const int32_t* sorted_ids,
+                          const int32_t* block_expert, const int32_t* n_post,
+                          void* h, int H, int I, int k, int bm, int max_rows,
+                          hipStream_t s);
+// y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows).
+hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
+                       const int32_t* block_expert, const int32_t* n_post,
+                       float* y, int H, int I, int bm, int max_rows,
+                       hipStream_t s);
+// out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), rounded once.
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
+                          const int32_t* slot_pos, int T, int H, int k,
+                          int n_shared, void* out, bool out_bf16,
+                          hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,154 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert-layer forward library.
+ *
+ * One MoE expert layer, forward only, on one GPU's share of a DP-attention +
+ * TP-MoE deployment ("DP Attention and TBO for DeepSeek-V4 on MI355X",
+ * summary page, opening section: DP attention with TP MoE joined by
+ * all_gather / reduce_scatter).  The input is the all-gathered token batch,
+ * padded to the largest DP rank (same page, PrefillDelayer section), and the
+ * experts are held with their intermediate dimension sliced as TP slices it,
+ * so `out` is this GPU's partial sum, ready for a reduce_scatter.
+ *
+ * Steps: router logits -> top-k + softmax over the selected logits (ties to
+ * the lower expert id) -> expert align (stable counting sort of the token /
+ * expert assignments, each expert padded to the GEMM block M) -> gate/up
+ * grouped GEMM with SiLU(gate)*up -> down grouped GEMM -> top-k-weighted
+ * combine ("[SGLang] Single Batch Overlap for MoE models": down-projection
+ * GEMM, then combine).  Optional always-on shared experts ("Step3 Inference
+ * Optimization on AMD Instinct MI308X", optimisation list: shared-expert MLP
+ * fused into the MoE layer) and fp8 e4m3 weights with 128x128 fp32 block
+ * scales (same list: FP8 blockscale; "AMD Instinct MI355X: ATOM ...":
+ * block-scale GEMM).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *    buffer; the library allocates no device memory and keeps no per-call
+ *    state, so calls on different streams with distinct workspaces may run
+ *    concurrently.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They never synchronise, so they may be captured in a graph.
+ *  - All arguments are validated before anything is launched; a non-zero
+ *    return means nothing was enqueued (except MOE_ERR_HIP, returned when a
+ *    launch itself fails).  Device faults surface at the caller's next
+ *    synchronisation.  Nothing is printed and no exception crosses the ABI.
+ *  - Layouts are dense row-major with the reduction (K) dimension contiguous;
+ *    every pointer must be 16-byte aligned.
+ *  - Rows with valid_rows[t] == 0 are never read (they may hold NaN).  Valid
+ *    rows must be finite.
+ */
+#ifndef MOE_AMD_H
+#define MOE_AMD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, size out of range, bad topk/block_m */
+  MOE_ERR_UNSUPPORTED = -2, /* dtype combination or shape the kernels do not cover */
+  MOE_ERR_WORKSPACE = -3,   /* workspace_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = -4          /* a HIP launch / runtime call failed */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+
+/* Layer descriptor (host struct).
+ *   T         gathered rows, padding rows included (>= 1)
+ *   H         hidden size (multiple of 64; of 128 with fp8 weights)
+ *   E         routed experts (1..256)
+ *   n_shared  always-on shared experts, 0 or 1; stored after the routed
+ *             experts at index E of w13 / w2; not covered by router_w
+ *   I         per-GPU expert intermediate size (multiple of 32; of 128 with
+ *             fp8 weights)
+ *   act_dtype dtype of x, router_w and out: MOE_F32 or MOE_BF16
+ *   w_dtype   dtype of w13 / w2: MOE_F32 (with F32 activations), MOE_BF16 or
+ *             MOE_FP8_E4M3 (both with BF16 activations)
+ *   w13_scale fp8 only: fp32 [E+n_shared, 2I/128, H/128] block scales
+ *   w2_scale  fp8 only: fp32 [E+n_shared, H/128, I/128] block scales
+ *   block_m   GEMM block rows used inside moe_forward; 0 = library default
+ */
+typedef struct moe_desc {
+  int32_t T, H, E, n_shared, I;
+  int32_t act_dtype, w_dtype;
+  const float* w13_scale;
+  const float* w2_scale;
+  int32_t block_m;
+} moe_desc;
+
+/* Bytes of workspace moe_forward / moe_route need for this layer and topk
+ * (host, pure).  Returns 0 if the descriptor is invalid. */
+size_t moe_workspace_size(const moe_desc* desc, int32_t topk);
+
+/* Router: logits l[t,e] = sum_h x[t,h] * router_w[e,h] (fp32 accumulation),
+ * then per valid row the topk experts of largest logit (ties to the lower
+ * expert id), in slots of descending logit, with weights = softmax over the
+ * selected logits (they sum to 1).  Padding rows get ids -1 and weights 0.
+ *   x            [T, H] act_dtype
+ *   valid_rows   [T] uint8 (0 = padding row) or NULL = all rows valid
+ *   router_w     [E, H] act_dtype
+ *   topk_ids     out [T, topk] int32
+ *   topk_w       out [T, topk] fp32
+ *   logits       out [T, E] fp32 or NULL (debug; padding rows get 0)
+ *   workspace    >= moe_workspace_size(desc, topk) bytes
+ * (Routing: "Step3 Inference Optimization on AMD Instinct MI308X",
+ * Background: top-3 of 48 experts.) */
+int moe_route(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+              const void* router_w, int32_t topk, int32_t* topk_ids,
+              float* topk_w, float* logits, void* workspace,
+              size_t workspace_bytes, moe_stream_t stream);
+
+/* Align: stable counting sort of the flat assignments a = t*topk + j by
+ * expert id.  Expert segments in ascending expert order, ascending a inside a
+ * segment; each segment padded with -1 to a multiple of block_m; experts with
+ * no assignment get no block; ids of -1 are skipped.
+ *   topk_ids        [T, topk] int32 (values in [0, E) or -1)
+ *   block_m         1..256
+ *   sorted_ids      out, capacity >= T*topk + E*(block_m-1) int32
+ *   block_expert    out, capacity >= that / block_m: expert of each block
+ *   expert_offsets  out [E+1] int32: padded segment starts, [E] = total
+ *   n_post_padded   out [1] int32: total padded length
+ * Only the first n_post_padded / n_post_padded/block_m entries are written.
+ * (Per-expert block granularity: "[SGLang] Single Batch Overlap for MoE
+ * models", combine signal section, one signal per 64-token block.) */
+int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
+              int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+              int32_t* expert_offsets, int32_t* n_post_padded,
+              moe_stream_t stream);
+
+/* The whole layer: route -> align -> gate/up GEMM with SiLU(g)*u -> down GEMM
+ * -> combine out[t] = sum_j w[t,j] * y_{ids[t,j]}(x_t) (+ shared experts with
+ * weight 1), accumulated in fp32 and rounded once to act_dtype.  `out` is
+ * fully overwritten; padding rows are set to 0.
+ *   w13  [E+n_shared, 2I, H]: gate rows 0..I-1, then up rows I..2I-1
+ *   w2   [E+n_shared, H, I]
+ *   (fp8: uint8 e4m3fn codes; W = code value * block scale)
+ *   out  [T, H] act_dtype (must not alias any input) */
+int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                const void* router_w, const void* w13, const void* w2,
+                int32_t topk, void* out, void* workspace,
+                size_t workspace_bytes, moe_stream_t stream);
+
+/* Message for a status code (host; static string). */
+const char* moe_status_str(int status);
+
+/* ---- measurement hooks (host; not for the serving path) ------------------
+ * When enabled, moe_forward records a hipEvent pair around each of its
+ * kernel launches on the call's stream.  moe_profile_read waits for the
+ * recorded events, writes the summed milliseconds and launch counts of each
+ * stage (index < moe_num_stages()) and clears the record.  Enabling creates
+ * events; it is meant for benchmarks only. */
+int moe_num_stages(void);
+const char* moe_stage_name(int stage);
+int moe_profile_enable(int enable);
+int moe_profile_read(double* stage_ms, int32_t* stage_launches, int32_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_AMD_H */

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import get_config, make_inputs
+from workloads.gen import random_small
+
+from .parity import TOL, compare, device_layer, log, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import expert_layer_moe_amd as moe
+    moe.load_library()
+    yield
+
+
+# ------------------------------------------------------------------ routing --
+def _exact_inputs(T, H, E, k, seed, dup=True, zero_router=False, valid_frac=1.0):
+    """x in {-2..2}, router in {-8..8} * 2^-6: every partial sum of a logit is
+    a multiple of 2^-6 below 2^11, hence exact in fp32 in any order."""
+    inp = random_small(T=T, H=H, E=E, k=k, I=32, seed=seed, valid_frac=valid_frac)
+    g = torch.Generator().manual_seed(seed)
+    inp.x = torch.randint(-2, 3, (T, H), generator=g).to(torch.bfloat16)
+    R = torch.randint(-8, 9, (E, H), generator=g).float() * 2.0 ** -6
+    if dup:
+        R[E - 1] = R[1]          # exact ties between expert 1 and E-1
+        R[E // 2] = R[0]
+    if zero_router:
+        R.zero_()
+    inp.router = R.to(torch.bfloat16)
+    return inp
+
+
+@pytest.mark.parametrize("T,H,E,k,vf,zero", [
+    (100, 256, 40, 5, 0.8, False),
+    (37, 7168, 48, 3, 1.0, False),
+    (70, 1024, 256, 8, 0.9, False),
+    (16, 256, 8, 2, 1.0, True),
+])
+def test_route_exact_arithmetic_bitwise(T, H, E, k, vf, zero):
+    inp = _exact_inputs(T, H, E, k, seed=T + E, zero_router=zero, valid_frac=vf)
+    layer = device_layer(inp)
+    xd = inp.x.cuda()
+    vd = None if inp.valid is None else inp.valid.cuda()
+    ids, w, lg = layer.route(xd, vd, logits=True)
+    torch.cuda.synchronize()
+    x64, R64 = oracle.to_f64(inp.x), oracle.to_f64(inp.router)
+    valid = None if inp.valid is None else inp.valid.numpy().astype(bool)
+    ids_o, w_o, l_o = oracle.route(x64, valid, R64, k)
+    assert np.array_equal(ids.cpu().numpy(), ids_o)
+    v = np.ones(T, bool) if valid is None else valid
+    assert np.array_equal(lg.cpu().double().numpy()[v], l_o[v])
+    assert np.abs(w.cpu().double().numpy() - w_o).max() <= 1e-6
+    if zero:
+        assert (ids.cpu().numpy() == np.arange(k)).all()
+
+
+# -------------------------------------------------------------------- align --
+def _random_ids(T, E, k, seed, pad_frac=0.1):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    ids[rng.random(T) < pad_frac] = -1
+    return ids
+
+
+def _gpu_align(ids, E, bm, stream=None):
+    import expert_layer_moe_amd as moe
+    T, k = ids.shape
+    cap = T * k + E * (bm - 1)
+    d = moe.make_desc(T, 64, E, 32)
+    idd = torch.from_numpy(ids).cuda()
+    s = torch.full((cap,), -7, dtype=torch.int32, device="cuda")
+    be = torch.full(((cap + bm - 1) // bm,), -7, dtype=torch.int32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    n = torch.empty(1, dtype=torch.int32, device="cuda")
+    moe.moe_align(d, idd, k, bm, s, be, off, n, stream)
+    return s, be, off, n
+
+
+@pytest.mark.parametrize("T,E,k,bm", [
+    (1, 4, 1, 32), (37, 9, 3, 1), (256, 48, 3, 32), (128, 256, 8, 16),
+    (1000, 64, 6, 64), (8192, 256, 8, 32), (8192, 48, 3, 128), (333, 200, 7, 256),
+])
+def test_align_bitwise(T, E, k, bm):
+    ids = _random_ids(T, E, k, seed=T * 7 + E)
+    s, be, off, n = _gpu_align(ids, E, bm)
+    torch.cuda.synchronize()
+    s_o, be_o, off_o, n_o = oracle.align(ids, E, bm)
+    n_g = int(n.item())
+    assert n_g == n_o
+    assert np.array_equal(s.cpu().numpy()[:n_g], s_o)
+    assert np.array_equal(be.cpu().numpy()[:n_g // bm], be_o)
+    assert np.array_equal(off.cpu().numpy(), off_o)
+
+
+def test_align_deterministic_across_repeats_and_streams():
+    ids = _random_ids(4096, 256, 8, seed=5)
+    ref = [t.cpu() for t in _gpu_align(ids, 256, 32)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(10):
+        with torch.cuda.stream(s1):
+            a = _gpu_align(ids, 256, 32, s1)
+        with torch.cuda.stream(s2):
+            b = _gpu_align(ids, 256, 32, s2)
+        torch.cuda.synchronize()
+        for x, y, r in zip(a, b, ref):
+            assert torch.equal(x.cpu(), r) and torch.equal(y.cpu(), r)
+
+
+# ------------------------------------------------------- small full layers --
+SMALL = [
+    dict(T=70, H=256, E=8, k=2, I=64),
+    dict(T=100, H=512, E=16, k=4, I=96, n_shared=1, valid_frac=0.7),
+    dict(T=90, H=256, E=6, k=2, I=128, w="fp8"),
+    dict(T=50, H=384, E=10, k=3, I=256, n_shared=1, w="fp8", valid_frac=0.6),
+    dict(T=33, H=128, E=5, k=2, I=32, act="f32", w="f32"),
+    dict(T=40, H=256, E=256, k=8, I=32),
+    dict(T=1, H=128, E=4, k=1, I=32),
+    dict(T=20, H=128, E=4, k=4, I=64),
+    dict(T=300, H=1024, E=32, k=4, I=160, valid_frac=0.5),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_small_layers_match_oracle(i):
+    kw = SMALL[i]
+    log(f"[case] small layer {i}: {kw}")
+    inp = random_small(seed=100 + i, **kw)
+    gpu = run_gpu(inp)
+    compare(inp, gpu)
+
+
+def test_all_rows_padding_gives_zero_output():
+    inp = random_small(T=40, H=256, E=8, k=2, I=64, seed=3)
+    inp.valid = torch.zeros(40, dtype=torch.uint8)
+    inp.x = torch.full_like(inp.x, float("nan"))
+    gpu = run_gpu(inp)
+    assert (gpu["out"] == 0).all() and (gpu["ids"] == -1).all()
+
+
+# ------------------------------------------------------ full-size workloads --
+@pytest.mark.parametrize("name", ["tiny", "decode_e48", "decode_e256_shared",
+                                  "gather_padded_e48", "prefill_ub_fp8"])
+def test_workload_matches_oracle(name):
+    cfg = get_config(name)
+    log(f"[case] {name}: generating inputs")
+    inp = make_inputs(cfg)
+    log(f"[case] {name}: GPU run")
+    gpu = run_gpu(inp)
+    log(f"[case] {name}: oracle run")
+    compare(inp, gpu)
+
+
+def test_gather_nan_padding_rows_are_never_read():
+    cfg = get_config("gather_padded_e48")
+    inp = make_inputs(cfg)
+    layer = device_layer(inp)
+    a = run_gpu(inp, layer)
+    x_nan = inp.x.clone()
+    x_nan[inp.valid == 0] = float("nan")
+    b = run_gpu(inp, layer, x=x_nan)
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["ids"], b["ids"])
+
+
+def test_prefill_two_streams_match_unsplit_batch():
+    """ub0 and ub1 (midpoint split) on two HIP streams give exactly the rows of
+    the unsplit 16384-row batch; ub1 also matches the oracle."""
+    cfg = get_config("prefill_ub_fp8")
+    full = make_inputs(cfg.with_(T=16384, ub=None))
+    layer = device_layer(full)
+    xd = full.x.cuda()
+    ref = layer.forward(xd)
+    s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
+    ws0, ws1 = layer.workspace(8192), torch.empty_like(layer.workspace(8192))
+    torch.cuda.synchronize()
+    outs = []
+    for s, ws, lo in ((s0, ws0, 0), (s1, ws1, 8192)):
+        with torch.cuda.stream(s):
+            outs.append(layer.forward(xd[lo:lo + 8192], workspace=ws, stream=s))
+    torch.cuda.synchronize()
+    both = torch.cat(outs)
+    assert torch.equal(both, ref), float((both.float() - ref.float()).abs().max())
+    ub1 = make_inputs(cfg.with_(ub=1))
+    gpu = dict(out=outs[1].float().cpu().double().numpy())
+    ids, w, lg = layer.route(ub1.x.cuda(), None, logits=True)
+    gpu.update(ids=ids.cpu().numpy(), w=w.cpu().double().numpy())
+    compare(ub1, gpu)
