@@ -1,0 +1,272 @@
+"""Benchmark of the MoE expert-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one moe_forward (router, top-k, align, gate/up GEMM + SiLU*mul,
+down GEMM, combine) over one batch of synthetic input already resident in
+HBM.  The default workload is the 48-expert top-3 decode share (256 gathered
+tokens, hidden 7168, inter 5120/8, bf16).  Prints one JSON line.
+
+Extra modes (used for profiling runs, not by the driver):
+  --config NAME       another workload (tiny, decode_e48, decode_e256_shared,
+                      gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8)
+  --no-cpu-baseline   skip the oracle timing
+  --copy-calibrate    time a plain 1 GiB device copy (for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s per MI355X + % of HBM-BW (decode) / MFMA peak (prefill)"
+PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "expert_layer_moe_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(cfg, ids, n_valid):
+    """Per-launch algorithmic bytes / flops of the expert kernels and of the
+    whole step: weights of touched experts only, valid rows only."""
+    import numpy as np
+    E, H, I, ns = cfg.E, cfg.H, cfg.I, cfg.n_shared
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w]
+    ab = 4 if cfg.act == "f32" else 2
+    touched = len(set(int(e) for e in np.unique(ids) if e >= 0)) + (ns if n_valid else 0)
+    n_assign = n_valid * (cfg.k + ns)
+    sc13 = sc2 = 0
+    if cfg.w == "fp8":
+        sc13 = touched * (2 * I // 128) * (H // 128) * 4
+        sc2 = touched * (H // 128) * (I // 128) * 4
+    w13 = touched * 2 * I * H * wb + sc13
+    w2 = touched * H * I * wb + sc2
+    x_bytes = n_valid * H * ab
+    out_bytes = cfg.T * H * ab
+    r_bytes = E * H * ab
+    return dict(
+        touched_experts=touched,
+        gate_up_bytes=w13 + x_bytes,
+        gate_up_flops=2.0 * n_assign * H * 2 * I,
+        down_bytes=w2,
+        down_flops=2.0 * n_assign * I * H,
+        step_bytes=w13 + w2 + x_bytes + out_bytes + r_bytes,
+        step_flops=2.0 * n_valid * H * E + 2.0 * n_assign * 3 * H * I,
+    )
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The oracle, as it stands, on the host cores (bounded sample)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cfg = inp.cfg
+    sample = inp
+    desc = f"whole {cfg.name} batch ({inp.n_valid} valid rows)"
+    if cfg.T > 1024:
+        from workloads.gen import LayerInputs
+        n = 512
+        sample = LayerInputs(cfg=cfg.with_(T=n), x=inp.x[:n],
+                             valid=None if inp.valid is None else inp.valid[:n],
+                             router=inp.router, w13=inp.w13, w2=inp.w2,
+                             s13=inp.s13, s2=inp.s2)
+        desc = f"first {n} rows of the {cfg.name} batch ({sample.n_valid} valid)"
+    times = []
+    t_end = time.time() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.moe_forward(sample)
+        times.append(time.perf_counter() - t0)
+        if time.time() > t_end or len(times) >= 5:
+            break
+    t = sorted(times)[len(times) // 2]
+    return {"value": round(sample.n_valid / t, 2), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{desc}; median of {len(times)} runs, {t:.2f} s each; "
+                      f"fp64 numpy/OpenBLAS oracle"}
+
+
+def traffic_for(kernel: str, workload: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{kernel}:{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def run(args):
+    import torch
+    import numpy as np
+    import expert_layer_moe_amd as moe
+    from workloads import get_config, make_inputs
+
+    moe.load_library()
+    if args.copy_calibrate:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return
+
+    pair = args.config == "prefill_pair_fp8"
+    cfg = get_config("prefill_ub_fp8" if pair else args.config)
+    log(f"[bench] generating {cfg.name}")
+    inp = make_inputs(cfg)
+    layer = moe.DeviceLayer(inp.router, inp.w13, inp.w2, cfg.k, cfg.n_shared,
+                            inp.s13, inp.s2)
+    x = inp.x.cuda()
+    valid = None if inp.valid is None else inp.valid.cuda()
+    out = torch.empty_like(x)
+    ws = layer.workspace(cfg.T)
+    streams = None
+    if pair:
+        ub1 = make_inputs(cfg.with_(ub=1))
+        x1 = ub1.x.cuda()
+        out1 = torch.empty_like(x1)
+        ws1 = torch.empty_like(ws)
+        streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    cur = torch.cuda.current_stream()
+
+    def step():
+        if not pair:
+            layer.forward(x, valid, out, ws)
+            return
+        ev = torch.cuda.Event()
+        ev.record(cur)
+        for s, xx, oo, ww in ((streams[0], x, out, ws), (streams[1], x1, out1, ws1)):
+            s.wait_event(ev)
+            with torch.cuda.stream(s):
+                layer.forward(xx, None, oo, ww, stream=s)
+        for s in streams:
+            cur.wait_stream(s)
+
+    ids, _, _ = layer.route(x, valid)
+    torch.cuda.synchronize()
+    n_valid = inp.n_valid
+    work = algorithmic_work(cfg, ids.cpu().numpy(), n_valid)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, with a HIP event pair around every kernel launch
+    # of moe_forward (recorded on the launch stream) for per-kernel durations
+    moe.moe_profile_enable(not pair)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(False)
+    ms_total = t0.elapsed_time(t1)
+    stages = moe.moe_profile_read()
+
+    # the same K steps without per-kernel events: event overhead check
+    torch.cuda.synchronize()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(args.steps):
+        step()
+    c1.record()
+    torch.cuda.synchronize()
+    ms_clean = c0.elapsed_time(c1)
+
+    ms_step = ms_total / args.steps
+    tokens_per_step = n_valid * (2 if pair else 1)
+    value = tokens_per_step / (ms_step / 1e3)
+    prefill = cfg.w == "fp8" or cfg.name.startswith("prefill")
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("prefill_pair_fp8" if pair else cfg.name),
+                   "T": cfg.T * (2 if pair else 1), "valid_rows": tokens_per_step,
+                   "H": cfg.H, "E": cfg.E, "topk": cfg.k, "I": cfg.I,
+                   "n_shared": cfg.n_shared, "weights": cfg.w,
+                   "two_streams": pair},
+    }
+    if not pair:
+        g_ms, g_n = stages["gate_up"]
+        d_ms, d_n = stages["down"]
+        dom = "gate_up"
+        avg_s = g_ms / max(g_n, 1) / 1e3
+        if prefill:
+            ach = work["gate_up_flops"] / avg_s / 1e12
+            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = work["gate_up_bytes"] / avg_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4)}
+        roof["kernel"] = dom
+        roof["kernel_avg_us"] = round(avg_s * 1e6, 2)
+        roof["traffic"] = traffic_for(dom, cfg.name)
+        res["roofline"] = roof
+        res["stages_us"] = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in stages.items()}
+        res["event_overhead_pct"] = round(100.0 * (ms_total - ms_clean) / ms_clean, 2)
+    step_s = ms_step / 1e3
+    res["step"] = {
+        "algorithmic_GB": round(work["step_bytes"] * (2 if pair else 1) / 1e9, 4),
+        "algorithmic_GFLOP": round(work["step_flops"] * (2 if pair else 1) / 1e9, 2),
+        "hbm_frac": round(work["step_bytes"] * (2 if pair else 1) / step_s / 1e9 / PEAK_HBM_GBPS, 4),
+        "mfma_frac": round(work["step_flops"] * (2 if pair else 1) / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "touched_experts": work["touched_experts"],
+        "ms_per_step_without_stage_events": round(ms_clean / args.steps, 5),
+    }
+    res["source_sha"] = source_sha()
+    if args.cpu_baseline and not pair:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode_e48")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--copy-calibrate", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in the design notes, not run",
+              file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()
