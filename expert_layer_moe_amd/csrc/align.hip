@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int ns, int bm,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
-    int32_t* __restrict__ slot_pos) {
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count) {
   __shared__ int cnt[kMaxSeg];
   __shared__ int base[kMaxSeg];
   __shared__ int wcnt[kAlignWaves][kMaxSeg];
@@ -98,6 +98,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // Sentinels at the tail of each segment, and the expert of each block.
   for (int seg = tid; seg < nseg; seg += kAlignThreads) {
     const int c = cnt[seg];
+    if (seg_count) seg_count[seg] = c;
     const int p = (c + bm - 1) / bm * bm;
     const int o = base[seg];
     for (int i = c; i < p; ++i) sorted_ids[o + i] = -1;
@@ -146,10 +147,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
-                        hipStream_t s) {
+                        int32_t* seg_count, hipStream_t s) {
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
                      E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
-                     slot_pos);
+                     slot_pos, seg_count);
   return hipGetLastError();
 }
 

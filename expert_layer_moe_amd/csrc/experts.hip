@@ -17,8 +17,6 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 32;  // rows per block in the MFMA kernels
-
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -36,116 +34,264 @@ __device__ __forceinline__ bf16x8 load_w8(const void* base, size_t elem_off) {
   }
 }
 
-// Gate/up: block = kBM sorted rows of one expert x 32 intermediate columns
-// (32 gate + the matching 32 up rows of W13).  4 waves in a 2x2 grid, each a
-// 16-row x 16-column tile of both gate and up.  grid = (max_blocks, I/32).
-template <bool FP8>
-__global__ __launch_bounds__(256) void gate_up_mfma_kernel(
+// The hardware hands block b to XCD b % 8.  Give each XCD a contiguous range
+// of logical block ids, so that the blocks of one expert (which read the same
+// token rows) share that XCD's L2.  nb must be a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  return (b & 7) * (nb >> 3) + (b >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming gate/up for expert segments of a few tiles of rows (the
+// decode regime, bound by HBM): one block per (expert, 4/KS groups of 16
+// intermediate columns).  The block's waves split K = H into KS contiguous
+// parts; a wave streams its part of 16 gate rows and the 16 matching up rows
+// of W13 exactly once per pass over up to MT 16-row tiles of the expert's
+// tokens, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
+// of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
+// grid.x = round_up(n_seg * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
+template <int KS, int MT, int KU, bool FP8>
+__global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ n_post,
-    uint16_t* __restrict__ h, int H, int I, int k) {
-  const int b = blockIdx.x;
-  if (b * kBM >= *n_post) return;
-  const int e = block_expert[b];
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    uint16_t* __restrict__ h, int H, int I, int k, int n_seg, int n_cg) {
+  constexpr int CGW = 4 / KS;
+  __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  if (lid >= n_seg * n_cg) return;
+  const int e = lid / n_cg, cgb = lid - e * n_cg;
+  const int cnt = seg_cnt[e];
+  if (cnt == 0) return;
+  const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int ks = wave % KS, cw = wave / KS;
+  const int cg = cgb * CGW + cw;
+  const bool col_ok = cg * 16 < I;
   const int m = lane % 16, g = lane / 16;
-  const int r = b * kBM + wr * 16 + m;
-  const int sid = sorted_ids[r];
-  const int tok = sid >= 0 ? sid / k : -1;
-  const int c0 = blockIdx.y * 32 + wc * 16;  // first gate column of this wave
-  const uint16_t* xa = x + (size_t)(tok >= 0 ? tok : 0) * H + 8 * g;
-  const size_t wg_off = ((size_t)e * 2 * I + c0 + m) * H + 8 * g;
+  const int klen = H / KS, kbeg = ks * klen;
+  const int c0 = col_ok ? cg * 16 : 0;
+  const size_t wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
   const size_t wu_off = wg_off + (size_t)I * H;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  floatx4 accg = {0.f, 0.f, 0.f, 0.f}, accu = accg;
-  if constexpr (!FP8) {
-#pragma unroll 4
-    for (int kk = 0; kk < H; kk += 32) {
-      const bf16x8 a = as_bf16x8(tok >= 0 ? ld16(xa + kk) : zero);
-      accg = mfma16x16x32(a, load_w8<false>(w13, wg_off + kk), accg);
-      accu = mfma16x16x32(a, load_w8<false>(w13, wu_off + kk), accu);
-    }
-  } else {
+  const float* sg = nullptr;
+  const float* su = nullptr;
+  if constexpr (FP8) {
     const int nkb = H / 128;
-    const float* sg = s13 + ((size_t)e * (2 * I / 128) + c0 / 128) * nkb;
-    const float* su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
-    for (int kb = 0; kb < nkb; ++kb) {
-      floatx4 pg = {0.f, 0.f, 0.f, 0.f}, pu = pg;
+    sg = s13 + ((size_t)e * (2 * I / 128) + c0 / 128) * nkb;
+    su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int ntiles = (cnt + 15) >> 4;
+  for (int t0 = 0; t0 < ntiles; t0 += MT) {
+    const uint16_t* xa[MT];
+    bool av[MT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kk = kb * 128 + q * 32;
-        const bf16x8 a = as_bf16x8(tok >= 0 ? ld16(xa + kk) : zero);
-        pg = mfma16x16x32(a, load_w8<true>(w13, wg_off + kk), pg);
-        pu = mfma16x16x32(a, load_w8<true>(w13, wu_off + kk), pu);
-      }
-      const float scg = sg[kb], scu = su[kb];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int rr = (t0 + mt) * 16 + m;
+      av[mt] = rr < cnt;
+      const int sid = av[mt] ? sorted_ids[row0 + rr] : 0;
+      xa[mt] = x + (size_t)(sid / k) * H + kbeg + 8 * g;
+    }
+    floatx4 ag[MT], au[MT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        accg[i] = fmaf(scg, pg[i], accg[i]);
-        accu[i] = fmaf(scu, pu[i], accu[i]);
+    for (int mt = 0; mt < MT; ++mt) {
+      ag[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      au[mt] = ag[mt];
+    }
+    if (col_ok) {
+      for (int kk = 0; kk < klen; kk += 32 * KU) {
+        bf16x8 bg[KU], bu[KU], a[KU][MT];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+          bg[u] = load_w8<FP8>(w13, wg_off + kk + 32 * u);
+          bu[u] = load_w8<FP8>(w13, wu_off + kk + 32 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            a[u][mt] = as_bf16x8((t0 + mt < ntiles && av[mt]) ? ld16(xa[mt] + kk + 32 * u) : zero);
+        if constexpr (FP8) {
+          floatx4 pg[MT], pu[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            pu[mt] = pg[mt];
+          }
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (t0 + mt < ntiles) {
+                pg[mt] = mfma16x16x32(a[u][mt], bg[u], pg[mt]);
+                pu[mt] = mfma16x16x32(a[u][mt], bu[u], pu[mt]);
+              }
+          const int kb = (kbeg + kk) >> 7;
+          const float scg = sg[kb], scu = su[kb];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ag[mt][i] = fmaf(scg, pg[mt][i], ag[mt][i]);
+              au[mt][i] = fmaf(scu, pu[mt][i], au[mt][i]);
+            }
+        } else {
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (t0 + mt < ntiles) {
+                ag[mt] = mfma16x16x32(a[u][mt], bg[u], ag[mt]);
+                au[mt] = mfma16x16x32(a[u][mt], bu[u], au[mt]);
+              }
+        }
       }
     }
-  }
+    if constexpr (KS == 1) {
+      if (col_ok) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = b * kBM + wr * 16 + 4 * g + i;
-    h[(size_t)row * I + c0 + m] = f32_to_bf16_bits(silu_mul(accg[i], accu[i]));
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = (t0 + mt) * 16 + 4 * g + i;
+            if (r < cnt)
+              h[(size_t)(row0 + r) * I + c0 + m] =
+                  f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
+          }
+      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        red[wave][0][mt][lane] = ag[mt];
+        red[wave][1][mt][lane] = au[mt];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if ((mt % KS) == ks && t0 + mt < ntiles && col_ok) {
+          floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
+#pragma unroll
+          for (int q = 1; q < KS; ++q) {
+            const floatx4 g2 = red[cw * KS + q][0][mt][lane];
+            const floatx4 u2 = red[cw * KS + q][1][mt][lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              G[i] += g2[i];
+              U[i] += u2[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = (t0 + mt) * 16 + 4 * g + i;
+            if (r < cnt)
+              h[(size_t)(row0 + r) * I + c0 + m] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
-// Down: block = kBM sorted rows x 64 output columns; 4 waves in a 2x2 grid,
-// each 16 rows x 32 columns (two MFMA tiles).  grid = (max_blocks, H/64).
-template <bool FP8>
-__global__ __launch_bounds__(256) void down_mfma_kernel(
+// Weight-streaming down projection: one block per (expert, 64*NT output
+// columns); each wave streams NT 16-row tiles of W2 (full K = I) once per pass
+// over up to MT 16-row tiles of the expert's h rows.  y rows are fp32.
+// grid.x = round_up(n_seg * n_ng, 8), n_ng = ceil(H / (64 * NT)).
+template <int MT, int NT, int KU, bool FP8>
+__global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
-    const float* __restrict__ s2, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ n_post, float* __restrict__ y, int H, int I) {
-  const int b = blockIdx.x;
-  if (b * kBM >= *n_post) return;
-  const int e = block_expert[b];
+    const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int I,
+    int n_seg, int n_ng) {
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  if (lid >= n_seg * n_ng) return;
+  const int e = lid / n_ng, ngb = lid - e * n_ng;
+  const int cnt = seg_cnt[e];
+  if (cnt == 0) return;
+  const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int wr = wave >> 1, wc = wave & 1;
+  const int n0 = (ngb * 4 + wave) * NT * 16;
+  if (n0 >= H) return;
   const int m = lane % 16, g = lane / 16;
-  const int r = b * kBM + wr * 16 + m;
-  const uint16_t* ha = h + (size_t)r * I + 8 * g;
-  const int n0 = blockIdx.y * 64 + wc * 32;
-  const size_t w0 = ((size_t)e * H + n0 + m) * I + 8 * g;
-  const size_t w1 = w0 + (size_t)16 * I;
-  floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-  if constexpr (!FP8) {
-#pragma unroll 4
-    for (int kk = 0; kk < I; kk += 32) {
-      const bf16x8 a = as_bf16x8(ld16(ha + kk));
-      acc0 = mfma16x16x32(a, load_w8<false>(w2, w0 + kk), acc0);
-      acc1 = mfma16x16x32(a, load_w8<false>(w2, w1 + kk), acc1);
-    }
-  } else {
-    const int nkb = I / 128;
-    const float* sc = s2 + ((size_t)e * (H / 128) + n0 / 128) * nkb;
-    for (int kb = 0; kb < nkb; ++kb) {
-      floatx4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = p0;
+  size_t wo[NT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int kk = kb * 128 + q * 32;
-        const bf16x8 a = as_bf16x8(ld16(ha + kk));
-        p0 = mfma16x16x32(a, load_w8<true>(w2, w0 + kk), p0);
-        p1 = mfma16x16x32(a, load_w8<true>(w2, w1 + kk), p1);
-      }
-      const float s = sc[kb];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc0[i] = fmaf(s, p0[i], acc0[i]);
-        acc1[i] = fmaf(s, p1[i], acc1[i]);
-      }
-    }
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = min(n0 + nt * 16, H - 16);
+    wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
   }
+  const float* sc = nullptr;
+  if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int ntiles = (cnt + 15) >> 4;
+  for (int t0 = 0; t0 < ntiles; t0 += MT) {
+    const uint16_t* ha[MT];
+    bool av[MT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t row = (size_t)(b * kBM + wr * 16 + 4 * g + i);
-    y[row * H + n0 + m] = acc0[i];
-    y[row * H + n0 + 16 + m] = acc1[i];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int rr = (t0 + mt) * 16 + m;
+      av[mt] = rr < cnt;
+      ha[mt] = h + (size_t)(row0 + (av[mt] ? rr : 0)) * I + 8 * g;
+    }
+    floatx4 acc[MT][NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < I; kk += 32 * KU) {
+      bf16x8 b[KU][NT], a[KU][MT];
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) b[u][nt] = load_w8<FP8>(w2, wo[nt] + kk + 32 * u);
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          a[u][mt] = as_bf16x8((t0 + mt < ntiles && av[mt]) ? ld16(ha[mt] + kk + 32 * u) : zero);
+      if constexpr (FP8) {
+        floatx4 p[MT][NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (t0 + mt < ntiles)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], p[mt][nt]);
+        const int kb = kk >> 7;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            if (t0 + mt < ntiles)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], acc[mt][nt]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + nt * 16 + m;
+        if (n0 + nt * 16 >= H) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = (t0 + mt) * 16 + 4 * g + i;
+          if (r < cnt) y[(size_t)(row0 + r) * H + n] = acc[mt][nt][i];
+        }
+      }
   }
 }
 
@@ -199,6 +345,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
     int H, int k, int ns, void* __restrict__ out, int out_bf16) {
   const int t = blockIdx.x;
+  const int nbeg = blockIdx.y * blockDim.x * 4;
+  const int nend = min(H, nbeg + (int)blockDim.x * 4);
   const bool valid = ids[(size_t)t * k] >= 0;
   const int kk = k + ns;
   int pos[kMaxSlots];
@@ -208,7 +356,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
     pos[j] = (valid && j < kk) ? slot_pos[(size_t)t * kk + j] : 0;
     wt[j] = (valid && j < k) ? w[(size_t)t * k + j] : 1.f;
   }
-  for (int n = threadIdx.x * 4; n < H; n += blockDim.x * 4) {
+  for (int n = nbeg + threadIdx.x * 4; n < nend; n += blockDim.x * 4) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     if (valid) {
 #pragma unroll
@@ -234,9 +382,55 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 }  // namespace
 
+namespace {
+
+int pick_ku(int len, bool fp8) {
+  // largest K-steps-per-batch in {4, 2, 1} that tiles len (fp8: a batch must
+  // stay inside one 128-wide scale block, which 32 * {1,2,4} does)
+  for (int ku = 4; ku > 1; ku >>= 1)
+    if (len % (32 * ku) == 0) return ku;
+  (void)fp8;
+  return 1;
+}
+
+template <int KS, int KU, bool FP8>
+void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const void* w13,
+               const float* s13, const int32_t* sorted_ids, const int32_t* seg_off,
+               const int32_t* seg_cnt, uint16_t* h, int H, int I, int k, int n_seg,
+               int n_cg) {
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8>), grid, dim3(256), 0, s, x,
+                     w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+}
+
+template <int KS, bool FP8>
+void launch_gu_ku(int ku, dim3 grid, hipStream_t s, const uint16_t* x, const void* w13,
+                  const float* s13, const int32_t* sorted_ids, const int32_t* seg_off,
+                  const int32_t* seg_cnt, uint16_t* h, int H, int I, int k, int n_seg,
+                  int n_cg) {
+  if (ku == 4)
+    launch_gu<KS, 4, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+  else if (ku == 2)
+    launch_gu<KS, 2, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+  else
+    launch_gu<KS, 1, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+}
+
+template <int KU, bool FP8>
+void launch_dn(dim3 grid, hipStream_t s, const uint16_t* h, const void* w2, const float* s2,
+               const int32_t* seg_off, const int32_t* seg_cnt, float* y, int H, int I,
+               int n_seg, int n_ng) {
+  hipLaunchKernelGGL((down_stream_kernel<4, 2, KU, FP8>), grid, dim3(256), 0, s, h, w2, s2,
+                     seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+}
+
+int round8(int v) { return (v + 7) / 8 * 8; }
+
+}  // namespace
+
 hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
+                          const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                           void* h, int H, int I, int k, int bm, int max_rows,
                           hipStream_t s) {
   if (wkind == W_F32) {
@@ -246,21 +440,32 @@ hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
                        k, bm);
     return hipGetLastError();
   }
-  if (bm != kBM) return hipErrorInvalidValue;
-  dim3 grid(max_rows / kBM, I / 32);
-  if (wkind == W_FP8)
-    hipLaunchKernelGGL(gate_up_mfma_kernel<true>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), w13, s13, sorted_ids,
-                       block_expert, n_post, static_cast<uint16_t*>(h), H, I, k);
-  else
-    hipLaunchKernelGGL(gate_up_mfma_kernel<false>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), w13, s13, sorted_ids,
-                       block_expert, n_post, static_cast<uint16_t*>(h), H, I, k);
+  const bool fp8 = wkind == W_FP8;
+  // K split across the block's waves: 4 parts when each part still holds
+  // whole 32-wide MFMA steps (and, for fp8, whole 128-wide scale blocks).
+  int ks = 4;
+  while (ks > 1 && (H % ks != 0 || (H / ks) % (fp8 ? 128 : 32) != 0)) ks >>= 1;
+  const int ku = pick_ku(H / ks, fp8);
+  const int cgw = 4 / ks;
+  const int n_cg = (I / 16 + cgw - 1) / cgw;
+  dim3 grid(round8(n_seg * n_cg));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+#define GU(KS, FP)                                                                     \
+  launch_gu_ku<KS, FP>(ku, grid, s, xb, w13, s13, sorted_ids, seg_off, seg_cnt, hb, H, \
+                       I, k, n_seg, n_cg)
+  if (fp8) {
+    if (ks == 4) GU(4, true); else if (ks == 2) GU(2, true); else GU(1, true);
+  } else {
+    if (ks == 4) GU(4, false); else if (ks == 2) GU(2, false); else GU(1, false);
+  }
+#undef GU
   return hipGetLastError();
 }
 
 hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
+                       const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                        float* y, int H, int I, int bm, int max_rows,
                        hipStream_t s) {
   if (wkind == W_F32) {
@@ -269,16 +474,20 @@ hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2
                        block_expert, n_post, y, H, I, bm);
     return hipGetLastError();
   }
-  if (bm != kBM) return hipErrorInvalidValue;
-  dim3 grid(max_rows / kBM, H / 64);
-  if (wkind == W_FP8)
-    hipLaunchKernelGGL(down_mfma_kernel<true>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(h), w2, s2, block_expert, n_post,
-                       y, H, I);
-  else
-    hipLaunchKernelGGL(down_mfma_kernel<false>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(h), w2, s2, block_expert, n_post,
-                       y, H, I);
+  const bool fp8 = wkind == W_FP8;
+  const int ku = pick_ku(I, fp8);
+  const int n_ng = (H + 127) / 128;
+  dim3 grid(round8(n_seg * n_ng));
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  if (fp8) {
+    if (ku == 4) launch_dn<4, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    else if (ku == 2) launch_dn<2, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    else launch_dn<1, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+  } else {
+    if (ku == 4) launch_dn<4, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    else if (ku == 2) launch_dn<2, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    else launch_dn<1, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+  }
   return hipGetLastError();
 }
 
@@ -286,7 +495,7 @@ hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, s, y, ids, w, slot_pos,
+  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, y, ids, w, slot_pos,
                      T, H, k, n_shared, out, out_bf16 ? 1 : 0);
   return hipGetLastError();
 }

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kMaxE = 256;
 constexpr int kMaxTopk = 16;
-constexpr int kDefaultBM = 32;
+constexpr int kDefaultBM = 16;
 constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -23,7 +23,7 @@ struct Plan {
   int bm, ks;
   int cap;  // capacity of the sorted row list (multiple of bm)
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
-      off_slot, off_h, off_y, total;
+      off_slot, off_cnt, off_h, off_y, total;
 };
 
 int check_desc(const moe_desc* d, int32_t topk) {
@@ -33,6 +33,7 @@ int check_desc(const moe_desc* d, int32_t topk) {
   if (d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
   if (topk < 1 || topk > d->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (d->block_m != 0 && d->block_m != kDefaultBM) return MOE_ERR_UNSUPPORTED;
+  if (d->act_dtype == MOE_BF16 && d->H % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32;
   const bool bf16 = d->act_dtype == MOE_BF16 && d->w_dtype == MOE_BF16;
   const bool fp8 = d->act_dtype == MOE_BF16 && d->w_dtype == MOE_FP8_E4M3;
@@ -79,6 +80,7 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_offs = take((size_t)(p->E + p->ns + 1) * 4);
   p->off_npost = take(4);
   p->off_slot = take((size_t)p->T * kk * 4);
+  p->off_cnt = take((size_t)(p->E + p->ns) * 4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
   p->off_y = take((size_t)p->cap * p->H * 4);
   p->total = o;
@@ -177,7 +179,7 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
     return MOE_ERR_INVALID_ARG;
   if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
-                        block_expert, expert_offsets, n_post_padded, nullptr,
+                        block_expert, expert_offsets, n_post_padded, nullptr, nullptr,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -202,6 +204,8 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   int32_t* offs = at<int32_t>(ws, p.off_offs);
   int32_t* npost = at<int32_t>(ws, p.off_npost);
   int32_t* slot = at<int32_t>(ws, p.off_slot);
+  int32_t* cnt = at<int32_t>(ws, p.off_cnt);
+  const int nseg = p.E + p.ns;
   void* h = at<void>(ws, p.off_h);
   float* y = at<float>(ws, p.off_y);
   const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
@@ -221,19 +225,19 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   {
     StageTimer tm(S_ALIGN, s);
     if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
-                          slot, s) != hipSuccess)
+                          slot, cnt, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_GATE_UP, s);
-    if (moe::launch_gate_up(wkind, x, w13, desc->w13_scale, sorted, bexp, npost, h,
-                            p.H, p.I, p.k, p.bm, p.cap, s) != hipSuccess)
+    if (moe::launch_gate_up(wkind, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
+                            cnt, nseg, h, p.H, p.I, p.k, p.bm, p.cap, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_DOWN, s);
-    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, y, p.H, p.I, p.bm,
-                         p.cap, s) != hipSuccess)
+    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg, y,
+                         p.H, p.I, p.bm, p.cap, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {

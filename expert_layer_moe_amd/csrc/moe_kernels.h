@@ -20,24 +20,29 @@ hipError_t launch_route_topk(const float* part, int ks, const uint8_t* valid,
 
 // ---- align -----------------------------------------------------------------
 // Stable counting sort of assignments by expert (n_shared extra always-on
-// segments of every valid row when n_shared > 0).  slot_pos may be null.
+// segments of every valid row when n_shared > 0).  slot_pos (position of each
+// assignment in the sorted list) and seg_count (unpadded rows per segment)
+// may be null.
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
-                        hipStream_t s);
+                        int32_t* seg_count, hipStream_t s);
 
 // ---- expert GEMMs ------------------------------------------------------------
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
 
-// h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r.
+// h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r
+// (segments seg_off[e] .. + seg_cnt[e] of the sorted list, e < n_seg).
 hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
+                          const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                           void* h, int H, int I, int k, int bm, int max_rows,
                           hipStream_t s);
 // y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows).
 hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
+                       const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                        float* y, int H, int I, int bm, int max_rows,
                        hipStream_t s);
 // out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), rounded once.
