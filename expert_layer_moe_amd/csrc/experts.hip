@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 // Weight-streaming down projection: one block per (expert, 64*NT output
 // columns); each wave streams NT 16-row tiles of W2 (full K = I) once per pass
 // over up to MT 16-row tiles of the expert's h rows.  y rows are fp32.
-// grid.x = round_up(n_seg * n_ng, 8), n_ng = ceil(H / (64 * NT)).
+// grid.x = round_up(n_seg * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
 template <int MT, int NT, int KU, bool FP8>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
@@ -419,7 +419,7 @@ template <int KU, bool FP8>
 void launch_dn(dim3 grid, hipStream_t s, const uint16_t* h, const void* w2, const float* s2,
                const int32_t* seg_off, const int32_t* seg_cnt, float* y, int H, int I,
                int n_seg, int n_ng) {
-  hipLaunchKernelGGL((down_stream_kernel<4, 2, KU, FP8>), grid, dim3(256), 0, s, h, w2, s2,
+  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8>), grid, dim3(256), 0, s, h, w2, s2,
                      seg_off, seg_cnt, y, H, I, n_seg, n_ng);
 }
 
@@ -476,7 +476,7 @@ hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2
   }
   const bool fp8 = wkind == W_FP8;
   const int ku = pick_ku(I, fp8);
-  const int n_ng = (H + 127) / 128;
+  const int n_ng = (H + 255) / 256;
   dim3 grid(round8(n_seg * n_ng));
   const uint16_t* hb = static_cast<const uint16_t*>(h);
   if (fp8) {

@@ -53,7 +53,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return __fdividef(g, 1.0f + __expf(-g)) * u;
 }
 
 }  // namespace moe

@@ -100,7 +100,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     taken[i] = e >= E;
     float s = 0.f;
     if (e < E) {
-      for (int z = 0; z < ks; ++z) s += part[((size_t)z * T + t) * E + e];
+      // fixed summation order z = 0, 1, ...; loads issued 8 at a time
+      const float* pp = part + (size_t)t * E + e;
+      const size_t zs = (size_t)T * E;
+      int z = 0;
+      for (; z + 8 <= ks; z += 8) {
+        float v8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v8[q] = pp[(z + q) * zs];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s += v8[q];
+      }
+      for (; z < ks; ++z) s += pp[z * zs];
       if (logits_out) logits_out[(size_t)t * E + e] = s;
     }
     v[i] = s;
