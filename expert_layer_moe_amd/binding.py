@@ -189,8 +189,16 @@ def stage_names():
     return [lib.moe_stage_name(i).decode() for i in range(lib.moe_num_stages())]
 
 
-def moe_profile_enable(on: bool):
-    _check(load_library().moe_profile_enable(1 if on else 0))
+def moe_profile_enable(stages=None):
+    """Time the named stages (None or [] = off, "all" = every stage)."""
+    if stages == "all":
+        mask = -1
+    else:
+        names = stage_names()
+        mask = 0
+        for s in stages or []:
+            mask |= 1 << names.index(s)
+    _check(load_library().moe_profile_enable(mask))
 
 
 def moe_profile_read():

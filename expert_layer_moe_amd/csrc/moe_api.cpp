@@ -102,7 +102,7 @@ struct ProfRecord {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+unsigned g_prof_mask = 0;  // bit s set: time stage s
 std::vector<ProfRecord> g_prof;
 
 struct StageTimer {
@@ -111,7 +111,7 @@ struct StageTimer {
   hipEvent_t a = nullptr, b = nullptr;
   StageTimer(int st, hipStream_t str) : stage(st), s(str) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
+    if (!(g_prof_mask >> st & 1u)) return;
     if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
       a = b = nullptr;
       return;
@@ -255,9 +255,9 @@ const char* moe_stage_name(int stage) {
   return (stage >= 0 && stage < S_COUNT) ? kStageNames[stage] : "";
 }
 
-int moe_profile_enable(int enable) {
+int moe_profile_enable(int stage_mask) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = enable != 0;
+  g_prof_mask = static_cast<unsigned>(stage_mask) & ((1u << S_COUNT) - 1u);
   return MOE_OK;
 }
 

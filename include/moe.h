@@ -138,14 +138,16 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
 const char* moe_status_str(int status);
 
 /* ---- measurement hooks (host; not for the serving path) ------------------
- * When enabled, moe_forward records a hipEvent pair around each of its
- * kernel launches on the call's stream.  moe_profile_read waits for the
- * recorded events, writes the summed milliseconds and launch counts of each
- * stage (index < moe_num_stages()) and clears the record.  Enabling creates
- * events; it is meant for benchmarks only. */
+ * moe_profile_enable(mask): for every stage s with bit s of mask set,
+ * moe_forward records a hipEvent pair around that stage's kernel launch on
+ * the call's stream (mask 0 = off, -1 = every stage).  moe_profile_read waits
+ * for the recorded events, writes the summed milliseconds and launch counts
+ * of each stage (index < moe_num_stages()) and clears the record.  Event
+ * records perturb the timeline slightly; enable only the stages you time.
+ * Recording creates events: benchmarks only. */
 int moe_num_stages(void);
 const char* moe_stage_name(int stage);
-int moe_profile_enable(int enable);
+int moe_profile_enable(int stage_mask);
 int moe_profile_read(double* stage_ms, int32_t* stage_launches, int32_t n);
 
 #ifdef __cplusplus
