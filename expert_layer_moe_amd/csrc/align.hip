@@ -21,6 +21,7 @@ namespace {
 constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 constexpr int kMaxSeg = 257;  // 256 routed experts + 1 shared
+constexpr int kBigTile = 128; // row tile of the GEMM kernels
 
 // Expert of assignment a in the virtual [T, k + n_shared] slot grid, or -1.
 // Slot k (when n_shared) is the shared expert E of every valid row (a row is
@@ -40,7 +41,9 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int T, int k, int E, int ns, int bm,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
-    int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count) {
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
+    int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
+    int32_t* __restrict__ n_tiles) {
   __shared__ int cnt[kMaxSeg];
   __shared__ int base[kMaxSeg];
   __shared__ int wcnt[kAlignWaves][kMaxSeg];
@@ -92,6 +95,34 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       offsets[nseg] = inc;
       *n_post = inc;
     }
+  } else if (wave == 1 && tile_seg != nullptr) {
+    // 128-row tiles of the segments with more than big_thr rows (handled by
+    // the tiled GEMM kernels), in segment order
+    int local[5];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int seg = lane * 5 + q;
+      const int c = seg < nseg ? cnt[seg] : 0;
+      local[q] = c > big_thr ? (c + kBigTile - 1) / kBigTile : 0;
+      sum += local[q];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      for (int i = 0; i < local[q]; ++i) {
+        tile_seg[run + i] = lane * 5 + q;
+        tile_row0[run + i] = i * kBigTile;
+      }
+      run += local[q];
+    }
+    if (lane == kWave - 1) *n_tiles = inc >= min_tiles ? inc : 0;
   }
   __syncthreads();
 
@@ -147,10 +178,11 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
-                        int32_t* seg_count, hipStream_t s) {
+                        int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
+                        int32_t* tile_row0, int32_t* n_tiles, hipStream_t s) {
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
                      E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
-                     slot_pos, seg_count);
+                     slot_pos, seg_count, big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
   return hipGetLastError();
 }
 

@@ -55,14 +55,15 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
-    uint16_t* __restrict__ h, int H, int I, int k, int n_seg, int n_cg) {
+    uint16_t* __restrict__ h, int H, int I, int k, int n_seg, int n_cg, int big_thr,
+    const int32_t* __restrict__ gemm_tiles) {
   constexpr int CGW = 4 / KS;
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   if (lid >= n_seg * n_cg) return;
   const int e = lid / n_cg, cgb = lid - e * n_cg;
   const int cnt = seg_cnt[e];
-  if (cnt == 0) return;
+  if (cnt == 0 || (cnt > big_thr && *gemm_tiles > 0)) return;   // the tiled GEMM's rows
   const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int ks = wave % KS, cw = wave / KS;
@@ -202,12 +203,12 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int I,
-    int n_seg, int n_ng) {
+    int n_seg, int n_ng, int big_thr, const int32_t* __restrict__ gemm_tiles) {
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   if (lid >= n_seg * n_ng) return;
   const int e = lid / n_ng, ngb = lid - e * n_ng;
   const int cnt = seg_cnt[e];
-  if (cnt == 0) return;
+  if (cnt == 0 || (cnt > big_thr && *gemm_tiles > 0)) return;   // the tiled GEMM's rows
   const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n0 = (ngb * 4 + wave) * NT * 16;
@@ -384,43 +385,60 @@ __global__ __launch_bounds__(256) void combine_kernel(
 
 namespace {
 
-int pick_ku(int len, bool fp8) {
-  // largest K-steps-per-batch in {4, 2, 1} that tiles len (fp8: a batch must
-  // stay inside one 128-wide scale block, which 32 * {1,2,4} does)
+int pick_ku(int len) {
+  // largest K-steps-per-batch in {4, 2, 1} that tiles len (a batch of
+  // 32 * {1,2,4} never straddles a 128-wide fp8 scale block)
   for (int ku = 4; ku > 1; ku >>= 1)
     if (len % (32 * ku) == 0) return ku;
-  (void)fp8;
   return 1;
 }
 
+struct GuArgs {
+  dim3 grid;
+  hipStream_t s;
+  const uint16_t* x;
+  const void* w13;
+  const float* s13;
+  const int32_t* sorted_ids;
+  const int32_t* seg_off;
+  const int32_t* seg_cnt;
+  uint16_t* h;
+  int H, I, k, n_seg, n_cg, big_thr;
+  const int32_t* gemm_tiles;
+};
+
 template <int KS, int KU, bool FP8>
-void launch_gu(dim3 grid, hipStream_t s, const uint16_t* x, const void* w13,
-               const float* s13, const int32_t* sorted_ids, const int32_t* seg_off,
-               const int32_t* seg_cnt, uint16_t* h, int H, int I, int k, int n_seg,
-               int n_cg) {
-  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8>), grid, dim3(256), 0, s, x,
-                     w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+void launch_gu(const GuArgs& a) {
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8>), a.grid, dim3(256), 0, a.s, a.x,
+                     a.w13, a.s13, a.sorted_ids, a.seg_off, a.seg_cnt, a.h, a.H, a.I, a.k,
+                     a.n_seg, a.n_cg, a.big_thr, a.gemm_tiles);
 }
 
 template <int KS, bool FP8>
-void launch_gu_ku(int ku, dim3 grid, hipStream_t s, const uint16_t* x, const void* w13,
-                  const float* s13, const int32_t* sorted_ids, const int32_t* seg_off,
-                  const int32_t* seg_cnt, uint16_t* h, int H, int I, int k, int n_seg,
-                  int n_cg) {
-  if (ku == 4)
-    launch_gu<KS, 4, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
-  else if (ku == 2)
-    launch_gu<KS, 2, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
-  else
-    launch_gu<KS, 1, FP8>(grid, s, x, w13, s13, sorted_ids, seg_off, seg_cnt, h, H, I, k, n_seg, n_cg);
+void launch_gu_ku(int ku, const GuArgs& a) {
+  if (ku == 4) launch_gu<KS, 4, FP8>(a);
+  else if (ku == 2) launch_gu<KS, 2, FP8>(a);
+  else launch_gu<KS, 1, FP8>(a);
 }
 
+struct DnArgs {
+  dim3 grid;
+  hipStream_t s;
+  const uint16_t* h;
+  const void* w2;
+  const float* s2;
+  const int32_t* seg_off;
+  const int32_t* seg_cnt;
+  float* y;
+  int H, I, n_seg, n_ng, big_thr;
+  const int32_t* gemm_tiles;
+};
+
 template <int KU, bool FP8>
-void launch_dn(dim3 grid, hipStream_t s, const uint16_t* h, const void* w2, const float* s2,
-               const int32_t* seg_off, const int32_t* seg_cnt, float* y, int H, int I,
-               int n_seg, int n_ng) {
-  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8>), grid, dim3(256), 0, s, h, w2, s2,
-                     seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+void launch_dn(const DnArgs& a) {
+  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
+                     a.s2, a.seg_off, a.seg_cnt, a.y, a.H, a.I, a.n_seg, a.n_ng, a.big_thr,
+                     a.gemm_tiles);
 }
 
 int round8(int v) { return (v + 7) / 8 * 8; }
@@ -431,8 +449,8 @@ hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
                           const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          void* h, int H, int I, int k, int bm, int max_rows,
-                          hipStream_t s) {
+                          int big_thr, const int32_t* gemm_tiles, void* h, int H, int I,
+                          int k, int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(gate_up_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(w13),
@@ -445,29 +463,29 @@ hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
   // whole 32-wide MFMA steps (and, for fp8, whole 128-wide scale blocks).
   int ks = 4;
   while (ks > 1 && (H % ks != 0 || (H / ks) % (fp8 ? 128 : 32) != 0)) ks >>= 1;
-  const int ku = pick_ku(H / ks, fp8);
+  const int ku = pick_ku(H / ks);
   const int cgw = 4 / ks;
   const int n_cg = (I / 16 + cgw - 1) / cgw;
-  dim3 grid(round8(n_seg * n_cg));
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  uint16_t* hb = static_cast<uint16_t*>(h);
-#define GU(KS, FP)                                                                     \
-  launch_gu_ku<KS, FP>(ku, grid, s, xb, w13, s13, sorted_ids, seg_off, seg_cnt, hb, H, \
-                       I, k, n_seg, n_cg)
+  GuArgs a{dim3(round8(n_seg * n_cg)), s, static_cast<const uint16_t*>(x), w13, s13,
+           sorted_ids, seg_off, seg_cnt, static_cast<uint16_t*>(h), H, I, k, n_seg, n_cg,
+           big_thr, gemm_tiles};
   if (fp8) {
-    if (ks == 4) GU(4, true); else if (ks == 2) GU(2, true); else GU(1, true);
+    if (ks == 4) launch_gu_ku<4, true>(ku, a);
+    else if (ks == 2) launch_gu_ku<2, true>(ku, a);
+    else launch_gu_ku<1, true>(ku, a);
   } else {
-    if (ks == 4) GU(4, false); else if (ks == 2) GU(2, false); else GU(1, false);
+    if (ks == 4) launch_gu_ku<4, false>(ku, a);
+    else if (ks == 2) launch_gu_ku<2, false>(ku, a);
+    else launch_gu_ku<1, false>(ku, a);
   }
-#undef GU
   return hipGetLastError();
 }
 
 hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                       float* y, int H, int I, int bm, int max_rows,
-                       hipStream_t s) {
+                       int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
+                       int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
@@ -475,18 +493,18 @@ hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2
     return hipGetLastError();
   }
   const bool fp8 = wkind == W_FP8;
-  const int ku = pick_ku(I, fp8);
+  const int ku = pick_ku(I);
   const int n_ng = (H + 255) / 256;
-  dim3 grid(round8(n_seg * n_ng));
-  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  DnArgs a{dim3(round8(n_seg * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2, seg_off,
+           seg_cnt, y, H, I, n_seg, n_ng, big_thr, gemm_tiles};
   if (fp8) {
-    if (ku == 4) launch_dn<4, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
-    else if (ku == 2) launch_dn<2, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
-    else launch_dn<1, true>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    if (ku == 4) launch_dn<4, true>(a);
+    else if (ku == 2) launch_dn<2, true>(a);
+    else launch_dn<1, true>(a);
   } else {
-    if (ku == 4) launch_dn<4, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
-    else if (ku == 2) launch_dn<2, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
-    else launch_dn<1, false>(grid, s, hb, w2, s2, seg_off, seg_cnt, y, H, I, n_seg, n_ng);
+    if (ku == 4) launch_dn<4, false>(a);
+    else if (ku == 2) launch_dn<2, false>(a);
+    else launch_dn<1, false>(a);
   }
   return hipGetLastError();
 }

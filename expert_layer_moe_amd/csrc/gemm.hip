@@ -1,0 +1,362 @@
+// LDS-tiled MFMA GEMMs for expert segments of many rows (the prefill regime,
+// bound by MFMA issue rather than by HBM), and for the router of large
+// batches.
+//
+// Prefill is compute-bound ("Step3 Inference Optimization on AMD Instinct
+// MI308X", results: prefill favours the part with more compute), so a block
+// works on a 128-row tile of one expert's rows against 256 weight rows:
+//   gate/up: 128 intermediate columns (128 gate rows + the matching 128 up
+//            rows of W13), epilogue h = SiLU(g) * u;
+//   down:    256 output columns (rows of W2), epilogue y (fp32);
+//   router:  256 experts (rows of R), epilogue logits (fp32).
+// 4 waves in a 2 x 2 grid; a wave owns 64 rows x 8 weight tiles of 16 rows
+// (32 MFMA 16x16x32 tiles; gate/up waves hold 4 gate tiles and the 4 matching
+// up tiles so SiLU * u is formed in registers).
+//
+// K runs in windows of 64.  Both operands of a window are staged through LDS
+// in MFMA fragment order: slot (16-row tile, step j) = 64 lanes x 16 B, lane
+// g*16 + r holding row r, K = 16 g + 8 j + (0..7) of the window (A and B use
+// the same K permutation).  Global loads run two windows ahead in registers
+// (window w+2 in flight while w is multiplied and w+1 is written to LDS), and
+// two LDS buffers alternate.  fp8 weights ("AMD Instinct MI355X: ATOM ...":
+// block-scale GEMM; Step3 page: FP8 blockscale) are dequantised once per block
+// while staged: value(q) * s in fp32, rounded to bf16.
+#include "moe_common.h"
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 128;   // rows per block tile
+constexpr int kBN = 256;   // weight rows per block tile
+constexpr int kKW = 64;    // K window
+constexpr int kASlots = kBM / 16 * 2;
+constexpr int kBSlots = kBN / 16 * 2;
+constexpr int kMaxScaleCols = kMaxGemmK / 128;   // fp8 scale blocks along K
+
+__device__ __forceinline__ int xcd_remap_g(int b, int nb) {
+  return (b & 7) * (nb >> 3) + (b >> 3);
+}
+
+enum GemmOp { OP_GATE_UP = 0, OP_DOWN = 1, OP_ROUTER = 2 };
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// 16 fp8 codes -> 16 bf16 (value * s, rounded), as two 16-byte halves
+__device__ __forceinline__ void fp8x16_scaled(u32x4 v, float s, u32x4& lo, u32x4& hi) {
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
+    out[2 * w] = pack_bf16x2(f01[0] * s, f01[1] * s);
+    out[2 * w + 1] = pack_bf16x2(f23[0] * s, f23[1] * s);
+  }
+  lo = u32x4{out[0], out[1], out[2], out[3]};
+  hi = u32x4{out[4], out[5], out[6], out[7]};
+}
+
+// Position of lane l's 16 bytes inside an LDS fragment slot of step j.  The
+// XOR keeps both the MFMA reads (8 consecutive lanes, fixed l/16) and the
+// staging writes (fixed row, 8 (l/16, j) pairs) on 8 distinct 16-byte bank
+// groups, so neither side conflicts.
+__device__ __forceinline__ int swz(int l, int j) { return l ^ (((l >> 4) << 1) | j); }
+
+// OP_GATE_UP: A = x rows of the tile's tokens (K = H); weight row wr < 128 is
+//   gate column nt*128 + wr, wr >= 128 the up column I + nt*128 + wr - 128.
+// OP_DOWN: A = h rows (K = I); weight rows nt*256 + wr of W2.
+// OP_ROUTER: A = x rows (padding rows enter as zeros, never used); weight
+//   rows nt*256 + wr of R.
+// Weight rows past the end are clamped to the last row: they feed only
+// output columns that are never stored.  grid.x = round_up(max_tiles * n_nt, 8).
+template <int OP, bool FP8>
+__global__ __launch_bounds__(256) void gemm_kernel(
+    const uint16_t* __restrict__ a_src, const void* __restrict__ w,
+    const float* __restrict__ wscale, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, const uint8_t* __restrict__ valid,
+    void* __restrict__ dst, int H, int I, int k, int n_nt, int max_tiles, int T, int E,
+    int ksplit) {
+  __shared__ u32x4 abuf[2][kASlots][kWave];   // 2 x 16 KB
+  __shared__ u32x4 bbuf[2][kBSlots][kWave];   // 2 x 32 KB
+  __shared__ float sscale[2][kMaxScaleCols];  // fp8: the two 128-row scale rows
+  const int lid0 = xcd_remap_g(blockIdx.x, gridDim.x);
+  const int per_z = max_tiles * n_nt;
+  if (lid0 >= per_z * ksplit) return;
+  const int z = lid0 / per_z, lid = lid0 - z * per_z;   // router: K chunk z
+  const int mt_id = lid / n_nt, nt = lid - mt_id * n_nt;
+  int e = 0, row_base, rows_here;
+  if constexpr (OP == OP_ROUTER) {
+    row_base = mt_id * kBM;
+    rows_here = min(kBM, T - row_base);
+  } else {
+    if (mt_id >= *n_tiles_ptr) return;
+    e = tile_seg[mt_id];
+    const int r0 = tile_row0[mt_id];
+    row_base = seg_off[e] + r0;        // first sorted row of the tile
+    rows_here = min(kBM, seg_cnt[e] - r0);
+  }
+  const int K = OP == OP_DOWN ? I : H;     // row stride of both operands
+  const int Kc = K / ksplit, kofs = z * Kc;  // this block's K range
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m = lane % 16, g = lane / 16;
+
+  // ---- A staging: 4 x 16 B per thread per window (row tid/8 + 32 s,
+  // 8-element piece tid%8 = K 16 (piece/2) + 8 (piece%2) of the window, i.e.
+  // lane group piece/2 of step piece%2); a wave instruction reads 8 rows x 128 B.
+  const int asq = tid & 7;
+  uint32_t aoff[4];
+  int aslot[4];
+  bool aon[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int row = (tid >> 3) + 32 * s;
+    const int rr = min(row, rows_here - 1);
+    size_t src_row;
+    if constexpr (OP == OP_GATE_UP) src_row = (size_t)(sorted_ids[row_base + rr] / k);
+    else src_row = (size_t)(row_base + rr);
+    aon[s] = true;
+    if constexpr (OP == OP_ROUTER) aon[s] = valid == nullptr || valid[src_row] != 0;
+    aoff[s] = (uint32_t)(src_row * K) + kofs + 8 * asq;
+    const int j = asq & 1, l = (asq >> 1) * 16 + (row & 15);
+    aslot[s] = ((row >> 4) * 2 + j) * kWave + swz(l, j);
+  }
+
+  if constexpr (OP == OP_ROUTER) {
+    if (!__syncthreads_or(aon[0] || aon[1] || aon[2] || aon[3])) return;
+  }
+
+  // ---- B staging.  fp8: 4 x 16 codes per thread (row tid/4 + 64 s, piece
+  // tid%4 = K 16 piece .. +15: lane group piece, steps 0 and 1); bf16: 8 x 8
+  // elements (row tid/8 + 32 s, piece tid%8 as for A).
+  constexpr int BP = FP8 ? 4 : 8;
+  const void* wexp;
+  uint32_t boff[BP];
+  int bslot[BP];
+  {
+    size_t base = 0;
+    if constexpr (OP == OP_GATE_UP) base = (size_t)e * 2 * I * H;
+    if constexpr (OP == OP_DOWN) base = (size_t)e * H * I;
+    wexp = FP8 ? static_cast<const void*>(static_cast<const uint8_t*>(w) + base)
+               : static_cast<const void*>(static_cast<const uint16_t*>(w) + base);
+#pragma unroll
+    for (int s = 0; s < BP; ++s) {
+      const int wr = FP8 ? (tid >> 2) + 64 * s : (tid >> 3) + 32 * s;
+      const int piece = FP8 ? (tid & 3) : (tid & 7);
+      int grow, nrows;
+      if constexpr (OP == OP_GATE_UP) {
+        grow = (wr < 128 ? 0 : I - 128) + nt * 128 + wr;
+        nrows = 2 * I;
+      } else {
+        grow = nt * kBN + wr;
+        nrows = OP == OP_DOWN ? H : E;
+      }
+      grow = min(grow, nrows - 1);
+      boff[s] = (uint32_t)grow * K + kofs + (FP8 ? 16 : 8) * piece;
+      const int j = FP8 ? 0 : (piece & 1), gq = FP8 ? piece : (piece >> 1);
+      bslot[s] = ((wr >> 4) * 2 + j) * kWave + swz(gq * 16 + (wr & 15), j);
+    }
+  }
+  // fp8: weight rows wr < 128 of the tile use scale row 0, the others row 1
+  // (gate/up: the gate and the up 128-row block; down: rows nt*256 + 0..255)
+  if constexpr (FP8) {
+    const int nkb = K / 128;
+    int sr0, sr1;
+    const float* sb;
+    if constexpr (OP == OP_GATE_UP) {
+      sb = wscale + (size_t)e * (2 * I / 128) * nkb;
+      sr0 = nt;
+      sr1 = I / 128 + nt;
+    } else {
+      sb = wscale + (size_t)e * (H / 128) * nkb;
+      sr0 = min(2 * nt, H / 128 - 1);
+      sr1 = min(2 * nt + 1, H / 128 - 1);
+    }
+    for (int i = tid; i < 2 * nkb; i += 256)
+      sscale[i / nkb][i % nkb] = sb[(size_t)(i < nkb ? sr0 : sr1) * nkb + i % nkb];
+  }
+
+  struct Stage {
+    u32x4 a[4];
+    u32x4 b[BP];
+  };
+  auto g_load = [&](Stage& S, int win) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      S.a[s] = *reinterpret_cast<const u32x4*>(a_src + aoff[s] + (uint32_t)win * kKW);
+#pragma unroll
+    for (int s = 0; s < BP; ++s) {
+      if constexpr (FP8)
+        S.b[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wexp) + boff[s] +
+                                                 (uint32_t)win * kKW);
+      else
+        S.b[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wexp) + boff[s] +
+                                                 (uint32_t)win * kKW);
+    }
+  };
+  auto l_store = [&](const Stage& S, int buf, int win) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) (&abuf[buf][0][0])[aslot[s]] = aon[s] ? S.a[s] : zero;
+#pragma unroll
+    for (int s = 0; s < BP; ++s) {
+      if constexpr (FP8) {
+        const float sc = sscale[s >> 1][win >> 1];
+        u32x4 lo, hi;
+        fp8x16_scaled(S.b[s], sc, lo, hi);
+        (&bbuf[buf][0][0])[bslot[s]] = lo;
+        (&bbuf[buf][0][0])[(bslot[s] + kWave) ^ 1] = hi;   // step 1: swz(l, 1)
+      } else {
+        (&bbuf[buf][0][0])[bslot[s]] = S.b[s];
+      }
+    }
+  };
+
+  floatx4 acc[4][8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[mt][q] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // LDS weight tile of wave column wn, tile q
+  auto btile = [&](int q) -> int {
+    if constexpr (OP == OP_GATE_UP) return (q < 4 ? 0 : 8) + wn * 4 + (q & 3);
+    else return wn * 8 + q;
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = swz(lane, j);
+      bf16x8 a[4], b[8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        a[mt] = __builtin_bit_cast(bf16x8, abuf[buf][(wm * 4 + mt) * 2 + j][p]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        b[q] = __builtin_bit_cast(bf16x8, bbuf[buf][btile(q) * 2 + j][p]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[mt][q] = mfma16x16x32(a[mt], b[q], acc[mt][q]);
+    }
+  };
+
+  // Two register stages (s0: even windows, s1: odd) and two LDS buffers;
+  // the window count is even (the launchers check K % 128 == 0).
+  // While window w is multiplied out of LDS, window w+1 waits in registers
+  // and window w+2 is in flight; loads past the last window re-read it (in
+  // bounds, never stored).  Fixed stage names keep the loop free of register
+  // copies, so the compiler waits only on the stage it stores.
+  const int nwin = Kc / kKW, last = nwin - 1;
+  Stage s0, s1;
+  g_load(s0, 0);
+  g_load(s1, min(1, last));
+  __syncthreads();   // scale rows
+  l_store(s0, 0, 0);
+  __syncthreads();
+  g_load(s0, min(2, last));
+  // sched_barrier(0) pins each stage's loads right after the barrier that
+  // frees its registers, a full window ahead of their LDS store.
+  for (int win = 0; win < nwin; win += 2) {
+    compute(0);
+    l_store(s1, 1, win + 1);
+    __syncthreads();
+    g_load(s1, min(win + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    l_store(s0, 0, win + 2);
+    __syncthreads();
+    g_load(s0, min(win + 4, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // epilogue: acc[mt][q] lane (m, g) element i = row wm*64 + mt*16 + 4g + i,
+  // column m of LDS weight tile btile(q)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 64 + mt * 16 + 4 * g + i;
+      if (row >= rows_here) continue;
+      if constexpr (OP == OP_GATE_UP) {
+        uint16_t* hr = static_cast<uint16_t*>(dst) + (size_t)(row_base + row) * I;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hr[nt * 128 + (wn * 4 + q) * 16 + m] =
+              f32_to_bf16_bits(silu_mul(acc[mt][q][i], acc[mt][q + 4][i]));
+      } else {
+        const int ncols = OP == OP_DOWN ? H : E;
+        float* yr = static_cast<float*>(dst) + (size_t)z * T * E + (size_t)(row_base + row) * ncols;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int n = nt * kBN + (wn * 8 + q) * 16 + m;
+          if (n < ncols) yr[n] = acc[mt][q][i];
+        }
+      }
+    }
+}
+
+int round8g(int v) { return (v + 7) / 8 * 8; }
+
+}  // namespace
+
+hipError_t launch_gate_up_gemm(bool fp8, const void* x, const void* w13, const float* s13,
+                               const int32_t* sorted_ids, const int32_t* tile_seg,
+                               const int32_t* tile_row0, const int32_t* n_tiles,
+                               const int32_t* seg_off, const int32_t* seg_cnt, void* h,
+                               int H, int I, int k, int max_tiles, hipStream_t s) {
+  if (H % 128 != 0 || I % 128 != 0 || H > kMaxGemmK) return hipErrorInvalidValue;
+  const int n_nt = I / 128;
+  dim3 grid(round8g(max_tiles * n_nt));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  if (fp8)
+    hipLaunchKernelGGL((gemm_kernel<OP_GATE_UP, true>), grid, dim3(256), 0, s, xb, w13, s13,
+                       sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, h,
+                       H, I, k, n_nt, max_tiles, 0, 0, 1);
+  else
+    hipLaunchKernelGGL((gemm_kernel<OP_GATE_UP, false>), grid, dim3(256), 0, s, xb, w13, s13,
+                       sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, h,
+                       H, I, k, n_nt, max_tiles, 0, 0, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_gemm(bool fp8, const void* h, const void* w2, const float* s2,
+                            const int32_t* tile_seg, const int32_t* tile_row0,
+                            const int32_t* n_tiles, const int32_t* seg_off,
+                            const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
+                            hipStream_t s) {
+  if (I % 128 != 0 || I > kMaxGemmK) return hipErrorInvalidValue;
+  const int n_nt = (H + kBN - 1) / kBN;
+  dim3 grid(round8g(max_tiles * n_nt));
+  const uint16_t* hb = static_cast<const uint16_t*>(h);
+  if (fp8)
+    hipLaunchKernelGGL((gemm_kernel<OP_DOWN, true>), grid, dim3(256), 0, s, hb, w2, s2, nullptr,
+                       tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, y, H, I, 1,
+                       n_nt, max_tiles, 0, 0, 1);
+  else
+    hipLaunchKernelGGL((gemm_kernel<OP_DOWN, false>), grid, dim3(256), 0, s, hb, w2, s2, nullptr,
+                       tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, y, H, I, 1,
+                       n_nt, max_tiles, 0, 0, 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
+                              float* part, int T, int H, int E, int ks, hipStream_t s) {
+  if (ks < 1 || H % (128 * ks) != 0) return hipErrorInvalidValue;
+  const int n_nt = (E + kBN - 1) / kBN;
+  const int tiles = (T + kBM - 1) / kBM;
+  dim3 grid(round8g(tiles * n_nt * ks));
+  hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false>), grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), R, nullptr, nullptr, nullptr, nullptr,
+                     nullptr, nullptr, nullptr, valid, part, H, 0, 1, n_nt, tiles, T, E, ks);
+  return hipGetLastError();
+}
+
+}  // namespace moe

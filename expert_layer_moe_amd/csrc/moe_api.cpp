@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: validation, workspace layout, launch sequence.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <mutex>
 #include <vector>
 
@@ -21,10 +22,19 @@ struct Plan {
   int T, H, E, ns, I, k;
   int act, w;
   int bm, ks;
-  int cap;  // capacity of the sorted row list (multiple of bm)
+  int cap;        // capacity of the sorted row list (multiple of bm)
+  bool router_gemm;  // tiled router GEMM (large batches) instead of the K split
+  int big_thr;    // segments with more rows go to the tiled GEMM kernels
+  int max_tiles;  // bound on their 128-row tiles
+  int min_tiles;  // fewer tiles than this stay on the streaming kernels
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
-      off_slot, off_cnt, off_h, off_y, total;
+      off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_h, off_y, total;
 };
+
+// Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
+// fragments reused across the tile) beat streaming the weights once per
+// 64-row pass.
+constexpr int kBigSegRows = 128;
 
 int check_desc(const moe_desc* d, int32_t topk) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
@@ -51,8 +61,21 @@ int check_desc(const moe_desc* d, int32_t topk) {
   return MOE_OK;
 }
 
+bool use_router_gemm(const moe_desc* d) {
+  return d->act_dtype == MOE_BF16 && d->T >= 1024 && d->H % 128 == 0;
+}
+
+// K split of the router logits (the top-k kernel sums the ks partials in a
+// fixed order).  The router GEMM's split depends on H only, so a row's logits
+// do not depend on the batch it comes in (a split batch reproduces the
+// unsplit one bit for bit).
 int choose_ks(const moe_desc* d) {
   if (d->act_dtype != MOE_BF16) return 1;
+  if (use_router_gemm(d)) {
+    int ks = 1;
+    while (ks < 8 && d->H % (128 * ks * 2) == 0) ks *= 2;
+    return ks;
+  }
   const int ksteps = d->H / 32;
   const long long base = (long long)((d->T + 15) / 16) * ((d->E + 63) / 64);
   int ks = 1;
@@ -67,7 +90,16 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->k = topk; p->act = d->act_dtype; p->w = d->w_dtype;
   p->bm = kDefaultBM;
   p->ks = choose_ks(d);
+  p->router_gemm = use_router_gemm(d);
+  p->big_thr = (d->act_dtype == MOE_BF16 && d->I % 128 == 0 && d->H <= moe::kMaxGemmK &&
+                d->I <= moe::kMaxGemmK)
+                   ? kBigSegRows
+                   : INT_MAX;
   const size_t kk = (size_t)topk + p->ns;
+  // the GEMM path only pays once its gate/up launch fills the chip
+  // (256 blocks of I/128 columns each)
+  p->min_tiles = (256 + p->I / 128 - 1) / (p->I / 128 > 0 ? p->I / 128 : 1);
+  p->max_tiles = (int)(((size_t)p->T * kk + 127) / 128 + p->E + p->ns);
   p->cap = (int)round_up((size_t)p->T * kk + (size_t)(p->E + p->ns) * (p->bm - 1), p->bm);
   const size_t act_h = (p->act == MOE_F32) ? 4 : 2;
   size_t o = 0;
@@ -81,6 +113,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_npost = take(4);
   p->off_slot = take((size_t)p->T * kk * 4);
   p->off_cnt = take((size_t)(p->E + p->ns) * 4);
+  p->off_tseg = take((size_t)p->max_tiles * 4);
+  p->off_trow = take((size_t)p->max_tiles * 4);
+  p->off_ntiles = take(4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
   p->off_y = take((size_t)p->cap * p->H * 4);
   p->total = o;
@@ -93,9 +128,12 @@ T* at(void* ws, size_t off) {
 }
 
 // ---- measurement hooks -------------------------------------------------------
-enum Stage { S_LOGITS = 0, S_TOPK, S_ALIGN, S_GATE_UP, S_DOWN, S_COMBINE, S_COUNT };
-const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align",
-                                    "gate_up", "down", "combine"};
+enum Stage {
+  S_LOGITS = 0, S_TOPK, S_ALIGN, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM, S_COMBINE,
+  S_COUNT
+};
+const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "gate_up",
+                                    "gate_up_gemm", "down", "down_gemm", "combine"};
 
 struct ProfRecord {
   int stage;
@@ -125,6 +163,14 @@ struct StageTimer {
     g_prof.push_back({stage, a, b});
   }
 };
+
+hipError_t launch_logits(const Plan& p, const void* x, const uint8_t* valid,
+                         const void* router_w, float* part, hipStream_t s) {
+  if (p.router_gemm)
+    return moe::launch_router_gemm(x, valid, router_w, part, p.T, p.H, p.E, p.ks, s);
+  return moe::launch_route_logits(p.act == MOE_BF16, x, valid, router_w, part, p.T, p.H, p.E,
+                                  p.ks, s);
+}
 
 }  // namespace
 
@@ -158,9 +204,7 @@ int moe_route(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* part = at<float>(workspace, p.off_part);
-  if (moe::launch_route_logits(p.act == MOE_BF16, x, valid_rows, router_w, part,
-                               p.T, p.H, p.E, p.ks, s) != hipSuccess)
-    return MOE_ERR_HIP;
+  if (launch_logits(p, x, valid_rows, router_w, part, s) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_route_topk(part, p.ks, valid_rows, p.T, p.E, p.k, topk_ids,
                              topk_w, logits, s) != hipSuccess)
     return MOE_ERR_HIP;
@@ -180,6 +224,7 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
   if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
                         block_expert, expert_offsets, n_post_padded, nullptr, nullptr,
+                        INT_MAX, 0, nullptr, nullptr, nullptr,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -205,6 +250,10 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   int32_t* npost = at<int32_t>(ws, p.off_npost);
   int32_t* slot = at<int32_t>(ws, p.off_slot);
   int32_t* cnt = at<int32_t>(ws, p.off_cnt);
+  int32_t* tseg = at<int32_t>(ws, p.off_tseg);
+  int32_t* trow = at<int32_t>(ws, p.off_trow);
+  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
+  const bool gemm = p.big_thr != INT_MAX;
   const int nseg = p.E + p.ns;
   void* h = at<void>(ws, p.off_h);
   float* y = at<float>(ws, p.off_y);
@@ -212,9 +261,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
 
   {
     StageTimer tm(S_LOGITS, s);
-    if (moe::launch_route_logits(p.act == MOE_BF16, x, valid_rows, router_w, part,
-                                 p.T, p.H, p.E, p.ks, s) != hipSuccess)
-      return MOE_ERR_HIP;
+    if (launch_logits(p, x, valid_rows, router_w, part, s) != hipSuccess) return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_TOPK, s);
@@ -225,19 +272,37 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   {
     StageTimer tm(S_ALIGN, s);
     if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
-                          slot, cnt, s) != hipSuccess)
+                          slot, cnt, p.big_thr, p.min_tiles, gemm ? tseg : nullptr, trow,
+                          ntiles,
+                          s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_GATE_UP, s);
     if (moe::launch_gate_up(wkind, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
-                            cnt, nseg, h, p.H, p.I, p.k, p.bm, p.cap, s) != hipSuccess)
+                            cnt, nseg, p.big_thr, gemm ? ntiles : nullptr, h, p.H, p.I, p.k,
+                            p.bm, p.cap,
+                            s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (gemm) {
+    StageTimer tm(S_GATE_UP_GEMM, s);
+    if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, x, w13, desc->w13_scale, sorted, tseg,
+                                 trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles,
+                                 s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_DOWN, s);
-    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg, y,
-                         p.H, p.I, p.bm, p.cap, s) != hipSuccess)
+    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg,
+                         p.big_thr, gemm ? ntiles : nullptr, y, p.H, p.I, p.bm, p.cap,
+                         s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (gemm) {
+    StageTimer tm(S_DOWN_GEMM, s);
+    if (moe::launch_down_gemm(wkind == moe::W_FP8, h, w2, desc->w2_scale, tseg, trow, ntiles,
+                              offs, cnt, y, p.H, p.I, p.max_tiles, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {

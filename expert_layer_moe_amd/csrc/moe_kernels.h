@@ -9,7 +9,8 @@ namespace moe {
 // ---- route -----------------------------------------------------------------
 // Partial router logits: part[z][t][e] = sum over the z-th K chunk of
 // x[t,:] * R[e,:].  bf16 inputs use MFMA; fp32 inputs use a plain FMA loop
-// (ks must be 1 then).  Rows with valid == 0 are not read and get 0.
+// (ks must be 1 then).  Rows with valid == 0 are not read; their partials
+// may be left unwritten (the top-k kernel never reads them).
 hipError_t launch_route_logits(bool bf16, const void* x, const uint8_t* valid,
                                const void* R, float* part, int T, int H, int E,
                                int ks, hipStream_t s);
@@ -23,28 +24,55 @@ hipError_t launch_route_topk(const float* part, int ks, const uint8_t* valid,
 // segments of every valid row when n_shared > 0).  slot_pos (position of each
 // assignment in the sorted list) and seg_count (unpadded rows per segment)
 // may be null.
+// With tile_seg non-null, also lists the 128-row tiles (segment, first row)
+// of every segment with more than big_thr rows, and their number; fewer
+// than min_tiles tiles (too few blocks to fill the chip) are dropped and
+// n_tiles is 0, leaving every segment to the streaming kernels.
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
-                        int32_t* seg_count, hipStream_t s);
+                        int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
+                        int32_t* tile_row0, int32_t* n_tiles, hipStream_t s);
 
 // ---- expert GEMMs ------------------------------------------------------------
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
 
+// Largest K (H for gate/up, I for down) the tiled GEMM kernels take (fp8:
+// their per-block table of 128-wide scale blocks).
+constexpr int kMaxGemmK = 16384;
+
 // h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r
 // (segments seg_off[e] .. + seg_cnt[e] of the sorted list, e < n_seg).
+// Segments with more than big_thr rows are skipped when *gemm_tiles > 0 (the
+// GEMM kernels' share); gemm_tiles may be null when big_thr is INT_MAX.
 hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
                           const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          void* h, int H, int I, int k, int bm, int max_rows,
-                          hipStream_t s);
+                          int big_thr, const int32_t* gemm_tiles, void* h, int H, int I,
+                          int k, int bm, int max_rows, hipStream_t s);
+// Tiled GEMMs for segments with more than big_thr rows (the align's tile
+// table), and the router GEMM for large batches.  K (H, I) % 128 == 0.
+hipError_t launch_gate_up_gemm(bool fp8, const void* x, const void* w13, const float* s13,
+                               const int32_t* sorted_ids, const int32_t* tile_seg,
+                               const int32_t* tile_row0, const int32_t* n_tiles,
+                               const int32_t* seg_off, const int32_t* seg_cnt, void* h,
+                               int H, int I, int k, int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm(bool fp8, const void* h, const void* w2, const float* s2,
+                            const int32_t* tile_seg, const int32_t* tile_row0,
+                            const int32_t* n_tiles, const int32_t* seg_off,
+                            const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
+                            hipStream_t s);
+// Router GEMM: part[z][t][e] for K chunk z of ks (H % (128 ks) == 0); tiles
+// with no valid row are skipped (their partials are never read).
+hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
+                              float* part, int T, int H, int E, int ks, hipStream_t s);
 // y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows).
 hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                       float* y, int H, int I, int bm, int max_rows,
-                       hipStream_t s);
+                       int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
+                       int bm, int max_rows, hipStream_t s);
 // out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), rounded once.
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,

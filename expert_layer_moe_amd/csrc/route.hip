@@ -28,6 +28,7 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(
   const int m = lane % 16, g = lane / 16;
   const int row = row0 + m;
   const bool rv = row < T && (valid == nullptr || valid[row] != 0);
+  if (__ballot(rv) == 0) return;   // no valid row: partials never read
   const int e = e0 + m;
   const bool ev = e < E;
   const int kb = blockIdx.z * kchunk;

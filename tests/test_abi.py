@@ -112,6 +112,6 @@ def test_workspace_grows_with_batch():
 
 def test_profile_hooks_without_records():
     assert moe.stage_names() == ["route_logits", "route_topk", "align", "gate_up",
-                                 "down", "combine"]
+                                 "gate_up_gemm", "down", "down_gemm", "combine"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())

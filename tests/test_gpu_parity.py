@@ -126,6 +126,11 @@ SMALL = [
     dict(T=1, H=128, E=4, k=1, I=32),
     dict(T=20, H=128, E=4, k=4, I=64),
     dict(T=300, H=1024, E=32, k=4, I=160, valid_frac=0.5),
+    # segments above 64 rows take the tiled GEMM kernels
+    dict(T=300, H=256, E=4, k=2, I=128),
+    dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
+    dict(T=1100, H=256, E=16, k=2, I=64, valid_frac=0.7),   # + router GEMM
+    dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),        # shared expert tiled
 ]
 
 
