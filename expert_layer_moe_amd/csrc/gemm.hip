@@ -15,8 +15,9 @@
 //
 // K runs in windows of 64.  Both operands of a window are staged through LDS
 // in MFMA fragment order: slot (16-row tile, step j) = 64 lanes x 16 B, lane
-// g*16 + r holding row r, K = 16 g + 8 j + (0..7) of the window (A and B use
-// the same K permutation).  Global loads run two windows ahead in registers
+// g*16 + r holding row r, K = 32 j + 8 g + (0..7) of the window.  Weights come
+// row-major or already in that order (fragment-packed, one contiguous 1 KB /
+// 512 B block per tile and step).  Global loads run two windows ahead in registers
 // (window w+2 in flight while w is multiplied and w+1 is written to LDS), and
 // two LDS buffers alternate.  fp8 weights ("AMD Instinct MI355X: ATOM ...":
 // block-scale GEMM; Step3 page: FP8 blockscale) are dequantised once per block
@@ -75,7 +76,7 @@ __device__ __forceinline__ int swz(int l, int j) { return l ^ (((l >> 4) << 1) |
 //   rows nt*256 + wr of R.
 // Weight rows past the end are clamped to the last row: they feed only
 // output columns that are never stored.  grid.x = round_up(max_tiles * n_nt, 8).
-template <int OP, bool FP8>
+template <int OP, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint16_t* __restrict__ a_src, const void* __restrict__ w,
     const float* __restrict__ wscale, const int32_t* __restrict__ sorted_ids,
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   const int m = lane % 16, g = lane / 16;
 
   // ---- A staging: 4 x 16 B per thread per window (row tid/8 + 32 s,
-  // 8-element piece tid%8 = K 16 (piece/2) + 8 (piece%2) of the window, i.e.
-  // lane group piece/2 of step piece%2); a wave instruction reads 8 rows x 128 B.
+  // 8-element piece tid%8 at K 8 piece = 32 j + 8 g of the window: lane group
+  // g of step j); a wave instruction reads 8 rows x 128 B.
   const int asq = tid & 7;
   uint32_t aoff[4];
   int aslot[4];
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     aon[s] = true;
     if constexpr (OP == OP_ROUTER) aon[s] = valid == nullptr || valid[src_row] != 0;
     aoff[s] = (uint32_t)(src_row * K) + kofs + 8 * asq;
-    const int j = asq & 1, l = (asq >> 1) * 16 + (row & 15);
+    const int j = asq >> 2, l = (asq & 3) * 16 + (row & 15);
     aslot[s] = ((row >> 4) * 2 + j) * kWave + swz(l, j);
   }
 
@@ -134,13 +135,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     if (!__syncthreads_or(aon[0] || aon[1] || aon[2] || aon[3])) return;
   }
 
-  // ---- B staging.  fp8: 4 x 16 codes per thread (row tid/4 + 64 s, piece
-  // tid%4 = K 16 piece .. +15: lane group piece, steps 0 and 1); bf16: 8 x 8
-  // elements (row tid/8 + 32 s, piece tid%8 as for A).
+  // ---- B staging: 16-byte pieces per thread per window, written to LDS
+  // slot (tile lt, step j) at the position of their lane.
+  //  row-major bf16: 8 pieces (row tid/8 + 32 s, 8 elements at K 8 (tid%8),
+  //    as for A);
+  //  row-major fp8: 4 pieces (row tid/4 + 64 s, 16 codes at K 16 p, p = tid%4:
+  //    lane groups 2 (p%2) and 2 (p%2) + 1 of step p/2);
+  //  fragment-packed (PW): piece P = 256 s + tid runs over the window's 32
+  //    fragment blocks (lt, j), 1 KB each in bf16 (one lane per piece) or
+  //    512 B in fp8 (two lanes per piece).
   constexpr int BP = FP8 ? 4 : 8;
+  constexpr uint32_t kWinStride = PW ? 1024 : kKW;   // elements per window
   const void* wexp;
   uint32_t boff[BP];
-  int bslot[BP];
+  int bslot[BP], bslot2[BP], bsr[BP];
   {
     size_t base = 0;
     if constexpr (OP == OP_GATE_UP) base = (size_t)e * 2 * I * H;
@@ -149,20 +157,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(
                : static_cast<const void*>(static_cast<const uint16_t*>(w) + base);
 #pragma unroll
     for (int s = 0; s < BP; ++s) {
-      const int wr = FP8 ? (tid >> 2) + 64 * s : (tid >> 3) + 32 * s;
-      const int piece = FP8 ? (tid & 3) : (tid & 7);
-      int grow, nrows;
-      if constexpr (OP == OP_GATE_UP) {
-        grow = (wr < 128 ? 0 : I - 128) + nt * 128 + wr;
-        nrows = 2 * I;
+      if constexpr (PW) {
+        const int P = 256 * s + tid;
+        const int blk = FP8 ? (P >> 5) : (P >> 6);
+        const int l0 = FP8 ? 2 * (P & 31) : (P & 63);
+        const int lt = blk >> 1, j = blk & 1;
+        int gt;   // 16-row tile of the expert's matrix
+        if constexpr (OP == OP_GATE_UP) gt = (lt < 8 ? 0 : I / 16 - 8) + nt * 8 + lt;
+        else gt = min(nt * 16 + lt, H / 16 - 1);
+        boff[s] = ((uint32_t)gt * (K / 32) + kofs / 32 + j) * 512 + 8 * l0;
+        bslot[s] = (lt * 2 + j) * kWave + swz(l0, j);
+        bslot2[s] = (lt * 2 + j) * kWave + swz(l0 + 1, j);
+        bsr[s] = lt >> 3;
       } else {
-        grow = nt * kBN + wr;
-        nrows = OP == OP_DOWN ? H : E;
+        const int wr = FP8 ? (tid >> 2) + 64 * s : (tid >> 3) + 32 * s;
+        const int piece = FP8 ? (tid & 3) : (tid & 7);
+        int grow, nrows;
+        if constexpr (OP == OP_GATE_UP) {
+          grow = (wr < 128 ? 0 : I - 128) + nt * 128 + wr;
+          nrows = 2 * I;
+        } else {
+          grow = nt * kBN + wr;
+          nrows = OP == OP_DOWN ? H : E;
+        }
+        grow = min(grow, nrows - 1);
+        boff[s] = (uint32_t)grow * K + kofs + (FP8 ? 16 : 8) * piece;
+        const int j = FP8 ? (piece >> 1) : (piece >> 2);
+        const int g0 = FP8 ? 2 * (piece & 1) : (piece & 3);
+        bslot[s] = ((wr >> 4) * 2 + j) * kWave + swz(g0 * 16 + (wr & 15), j);
+        bslot2[s] = ((wr >> 4) * 2 + j) * kWave + swz((g0 + 1) * 16 + (wr & 15), j);
+        bsr[s] = wr >> 7;
       }
-      grow = min(grow, nrows - 1);
-      boff[s] = (uint32_t)grow * K + kofs + (FP8 ? 16 : 8) * piece;
-      const int j = FP8 ? 0 : (piece & 1), gq = FP8 ? piece : (piece >> 1);
-      bslot[s] = ((wr >> 4) * 2 + j) * kWave + swz(gq * 16 + (wr & 15), j);
     }
   }
   // fp8: weight rows wr < 128 of the tile use scale row 0, the others row 1
@@ -196,10 +221,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     for (int s = 0; s < BP; ++s) {
       if constexpr (FP8)
         S.b[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(wexp) + boff[s] +
-                                                 (uint32_t)win * kKW);
+                                                 (uint32_t)win * kWinStride);
       else
         S.b[s] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(wexp) + boff[s] +
-                                                 (uint32_t)win * kKW);
+                                                 (uint32_t)win * kWinStride);
     }
   };
   auto l_store = [&](const Stage& S, int buf, int win) {
@@ -209,11 +234,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
     for (int s = 0; s < BP; ++s) {
       if constexpr (FP8) {
-        const float sc = sscale[s >> 1][win >> 1];
+        const float sc = sscale[bsr[s]][win >> 1];
         u32x4 lo, hi;
         fp8x16_scaled(S.b[s], sc, lo, hi);
         (&bbuf[buf][0][0])[bslot[s]] = lo;
-        (&bbuf[buf][0][0])[(bslot[s] + kWave) ^ 1] = hi;   // step 1: swz(l, 1)
+        (&bbuf[buf][0][0])[bslot2[s]] = hi;
       } else {
         (&bbuf[buf][0][0])[bslot[s]] = S.b[s];
       }
@@ -305,45 +330,60 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 
 int round8g(int v) { return (v + 7) / 8 * 8; }
 
+template <int OP, bool FP8, bool PW>
+void launch_gemm(dim3 grid, hipStream_t s, const uint16_t* a, const void* w, const float* ws,
+                 const int32_t* sorted_ids, const int32_t* tseg, const int32_t* trow,
+                 const int32_t* ntiles, const int32_t* seg_off, const int32_t* seg_cnt,
+                 void* dst, int H, int I, int k, int n_nt, int max_tiles) {
+  hipLaunchKernelGGL((gemm_kernel<OP, FP8, PW>), grid, dim3(256), 0, s, a, w, ws, sorted_ids,
+                     tseg, trow, ntiles, seg_off, seg_cnt, nullptr, dst, H, I, k, n_nt,
+                     max_tiles, 0, 0, 1);
+}
+
+template <int OP>
+void launch_gemm_w(bool fp8, bool packed, dim3 grid, hipStream_t s, const uint16_t* a,
+                   const void* w, const float* ws, const int32_t* sorted_ids,
+                   const int32_t* tseg, const int32_t* trow, const int32_t* ntiles,
+                   const int32_t* seg_off, const int32_t* seg_cnt, void* dst, int H, int I,
+                   int k, int n_nt, int max_tiles) {
+#define MOE_GEMM_ARGS grid, s, a, w, ws, sorted_ids, tseg, trow, ntiles, seg_off, seg_cnt, dst, \
+                      H, I, k, n_nt, max_tiles
+  if (fp8) {
+    if (packed) launch_gemm<OP, true, true>(MOE_GEMM_ARGS);
+    else launch_gemm<OP, true, false>(MOE_GEMM_ARGS);
+  } else {
+    if (packed) launch_gemm<OP, false, true>(MOE_GEMM_ARGS);
+    else launch_gemm<OP, false, false>(MOE_GEMM_ARGS);
+  }
+#undef MOE_GEMM_ARGS
+}
+
 }  // namespace
 
-hipError_t launch_gate_up_gemm(bool fp8, const void* x, const void* w13, const float* s13,
-                               const int32_t* sorted_ids, const int32_t* tile_seg,
-                               const int32_t* tile_row0, const int32_t* n_tiles,
-                               const int32_t* seg_off, const int32_t* seg_cnt, void* h,
-                               int H, int I, int k, int max_tiles, hipStream_t s) {
+hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void* w13,
+                               const float* s13, const int32_t* sorted_ids,
+                               const int32_t* tile_seg, const int32_t* tile_row0,
+                               const int32_t* n_tiles, const int32_t* seg_off,
+                               const int32_t* seg_cnt, void* h, int H, int I, int k,
+                               int max_tiles, hipStream_t s) {
   if (H % 128 != 0 || I % 128 != 0 || H > kMaxGemmK) return hipErrorInvalidValue;
   const int n_nt = I / 128;
-  dim3 grid(round8g(max_tiles * n_nt));
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (fp8)
-    hipLaunchKernelGGL((gemm_kernel<OP_GATE_UP, true>), grid, dim3(256), 0, s, xb, w13, s13,
-                       sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, h,
-                       H, I, k, n_nt, max_tiles, 0, 0, 1);
-  else
-    hipLaunchKernelGGL((gemm_kernel<OP_GATE_UP, false>), grid, dim3(256), 0, s, xb, w13, s13,
-                       sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, h,
-                       H, I, k, n_nt, max_tiles, 0, 0, 1);
+  launch_gemm_w<OP_GATE_UP>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
+                            static_cast<const uint16_t*>(x), w13, s13, sorted_ids, tile_seg,
+                            tile_row0, n_tiles, seg_off, seg_cnt, h, H, I, k, n_nt, max_tiles);
   return hipGetLastError();
 }
 
-hipError_t launch_down_gemm(bool fp8, const void* h, const void* w2, const float* s2,
-                            const int32_t* tile_seg, const int32_t* tile_row0,
+hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2,
+                            const float* s2, const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
                             const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
                             hipStream_t s) {
   if (I % 128 != 0 || I > kMaxGemmK) return hipErrorInvalidValue;
   const int n_nt = (H + kBN - 1) / kBN;
-  dim3 grid(round8g(max_tiles * n_nt));
-  const uint16_t* hb = static_cast<const uint16_t*>(h);
-  if (fp8)
-    hipLaunchKernelGGL((gemm_kernel<OP_DOWN, true>), grid, dim3(256), 0, s, hb, w2, s2, nullptr,
-                       tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, y, H, I, 1,
-                       n_nt, max_tiles, 0, 0, 1);
-  else
-    hipLaunchKernelGGL((gemm_kernel<OP_DOWN, false>), grid, dim3(256), 0, s, hb, w2, s2, nullptr,
-                       tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, nullptr, y, H, I, 1,
-                       n_nt, max_tiles, 0, 0, 1);
+  launch_gemm_w<OP_DOWN>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
+                         static_cast<const uint16_t*>(h), w2, s2, nullptr, tile_seg, tile_row0,
+                         n_tiles, seg_off, seg_cnt, y, H, I, 1, n_nt, max_tiles);
   return hipGetLastError();
 }
 
@@ -353,7 +393,7 @@ hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R
   const int n_nt = (E + kBN - 1) / kBN;
   const int tiles = (T + kBM - 1) / kBM;
   dim3 grid(round8g(tiles * n_nt * ks));
-  hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false, false>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), R, nullptr, nullptr, nullptr, nullptr,
                      nullptr, nullptr, nullptr, valid, part, H, 0, 1, n_nt, tiles, T, E, ks);
   return hipGetLastError();

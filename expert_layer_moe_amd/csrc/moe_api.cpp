@@ -36,13 +36,16 @@ struct Plan {
 // 64-row pass.
 constexpr int kBigSegRows = 128;
 
-int check_desc(const moe_desc* d, int32_t topk) {
+int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
   if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->E > kMaxE)
     return MOE_ERR_INVALID_ARG;
   if (d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
   if (topk < 1 || topk > d->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (d->block_m != 0 && d->block_m != kDefaultBM) return MOE_ERR_UNSUPPORTED;
+  if (d->w_layout != MOE_LAYOUT_ROW_MAJOR && d->w_layout != MOE_LAYOUT_FRAG16)
+    return MOE_ERR_INVALID_ARG;
+  if (d->w_layout == MOE_LAYOUT_FRAG16 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (d->act_dtype == MOE_BF16 && d->H % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const bool f32 = d->act_dtype == MOE_F32 && d->w_dtype == MOE_F32;
   const bool bf16 = d->act_dtype == MOE_BF16 && d->w_dtype == MOE_BF16;
@@ -51,7 +54,8 @@ int check_desc(const moe_desc* d, int32_t topk) {
   if (d->H % 64 != 0 || d->I % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (fp8) {
     if (d->H % 128 != 0 || d->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
-    if (d->w13_scale == nullptr || d->w2_scale == nullptr) return MOE_ERR_INVALID_ARG;
+    if (need_scales && (d->w13_scale == nullptr || d->w2_scale == nullptr))
+      return MOE_ERR_INVALID_ARG;
   }
   // sizes must fit the kernels' 32-bit row/element indexing of the row list
   const long long rows = (long long)d->T * (topk + d->n_shared) +
@@ -117,6 +121,8 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_trow = take((size_t)p->max_tiles * 4);
   p->off_ntiles = take(4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
+  // y (fp32 rows) also holds the packed token rows of the streaming gate/up
+  // (cap x H bf16) until the down kernels overwrite it
   p->off_y = take((size_t)p->cap * p->H * 4);
   p->total = o;
   return MOE_OK;
@@ -129,10 +135,10 @@ T* at(void* ws, size_t off) {
 
 // ---- measurement hooks -------------------------------------------------------
 enum Stage {
-  S_LOGITS = 0, S_TOPK, S_ALIGN, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM, S_COMBINE,
-  S_COUNT
+  S_LOGITS = 0, S_TOPK, S_ALIGN, S_PACK_X, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM,
+  S_COMBINE, S_COUNT
 };
-const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "gate_up",
+const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "pack_x", "gate_up",
                                     "gate_up_gemm", "down", "down_gemm", "combine"};
 
 struct ProfRecord {
@@ -180,6 +186,23 @@ size_t moe_workspace_size(const moe_desc* desc, int32_t topk) {
   Plan p;
   if (make_plan(desc, topk, &p) != MOE_OK) return 0;
   return p.total;
+}
+
+int moe_pack_weights(const moe_desc* desc, const void* w13, const void* w2, void* w13_packed,
+                     void* w2_packed, moe_stream_t stream) {
+  if (desc == nullptr) return MOE_ERR_INVALID_ARG;
+  moe_desc d = *desc;
+  d.w_layout = MOE_LAYOUT_FRAG16;
+  const int st = check_desc(&d, 1, /*need_scales=*/false);
+  if (st != MOE_OK) return st;
+  if (!w13 || !w2 || !w13_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
+  const int wkind = d.w_dtype == MOE_BF16 ? moe::W_BF16 : moe::W_FP8;
+  const size_t ne = (size_t)d.E + d.n_shared;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (moe::launch_pack_weights(wkind, w13, w13_packed, ne * 2 * d.I, d.H, s) != hipSuccess ||
+      moe::launch_pack_weights(wkind, w2, w2_packed, ne * d.H, d.I, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 const char* moe_status_str(int status) {
@@ -258,6 +281,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   void* h = at<void>(ws, p.off_h);
   float* y = at<float>(ws, p.off_y);
   const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
+  const bool packed = desc->w_layout == MOE_LAYOUT_FRAG16;
 
   {
     StageTimer tm(S_LOGITS, s);
@@ -277,31 +301,37 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
                           s) != hipSuccess)
       return MOE_ERR_HIP;
   }
+  if (wkind != moe::W_F32) {
+    StageTimer tm(S_PACK_X, s);
+    if (moe::launch_pack_x(x, sorted, bexp, npost, cnt, p.big_thr, gemm ? ntiles : nullptr, y,
+                           p.H, p.k, p.bm, p.cap, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
   {
     StageTimer tm(S_GATE_UP, s);
-    if (moe::launch_gate_up(wkind, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
-                            cnt, nseg, p.big_thr, gemm ? ntiles : nullptr, h, p.H, p.I, p.k,
-                            p.bm, p.cap,
+    if (moe::launch_gate_up(wkind, packed, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
+                            cnt, nseg, p.big_thr, gemm ? ntiles : nullptr, y, h, p.H, p.I,
+                            p.k, p.bm, p.cap,
                             s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   if (gemm) {
     StageTimer tm(S_GATE_UP_GEMM, s);
-    if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, x, w13, desc->w13_scale, sorted, tseg,
+    if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, packed, x, w13, desc->w13_scale, sorted, tseg,
                                  trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles,
                                  s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_DOWN, s);
-    if (moe::launch_down(wkind, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg,
+    if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg,
                          p.big_thr, gemm ? ntiles : nullptr, y, p.H, p.I, p.bm, p.cap,
                          s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   if (gemm) {
     StageTimer tm(S_DOWN_GEMM, s);
-    if (moe::launch_down_gemm(wkind == moe::W_FP8, h, w2, desc->w2_scale, tseg, trow, ntiles,
+    if (moe::launch_down_gemm(wkind == moe::W_FP8, packed, h, w2, desc->w2_scale, tseg, trow, ntiles,
                               offs, cnt, y, p.H, p.I, p.max_tiles, s) != hipSuccess)
       return MOE_ERR_HIP;
   }

@@ -41,24 +41,35 @@ enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
 // their per-block table of 128-wide scale blocks).
 constexpr int kMaxGemmK = 16384;
 
+// bf16 streaming path: x rows of the sorted rows of the streaming kernels'
+// segments, packed in MFMA fragment order into xp (max_rows x H bf16, 16-row
+// tiles; padding rows 0).  bm must be 16.
+hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
+                         const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
+                         const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
+                         int max_rows, hipStream_t s);
 // h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r
 // (segments seg_off[e] .. + seg_cnt[e] of the sorted list, e < n_seg).
 // Segments with more than big_thr rows are skipped when *gemm_tiles > 0 (the
 // GEMM kernels' share); gemm_tiles may be null when big_thr is INT_MAX.
-hipError_t launch_gate_up(int wkind, const void* x, const void* w13,
+// bf16: the token rows come from xp (launch_pack_x), and h rows of the
+// streaming kernels' segments are written in fragment order too (16-row
+// tiles; the GEMM kernels' rows stay row-major).  fp32 reads x directly.
+hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
                           const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          int big_thr, const int32_t* gemm_tiles, void* h, int H, int I,
-                          int k, int bm, int max_rows, hipStream_t s);
+                          int big_thr, const int32_t* gemm_tiles, const void* xp, void* h,
+                          int H, int I, int k, int bm, int max_rows, hipStream_t s);
 // Tiled GEMMs for segments with more than big_thr rows (the align's tile
 // table), and the router GEMM for large batches.  K (H, I) % 128 == 0.
-hipError_t launch_gate_up_gemm(bool fp8, const void* x, const void* w13, const float* s13,
-                               const int32_t* sorted_ids, const int32_t* tile_seg,
-                               const int32_t* tile_row0, const int32_t* n_tiles,
-                               const int32_t* seg_off, const int32_t* seg_cnt, void* h,
-                               int H, int I, int k, int max_tiles, hipStream_t s);
-hipError_t launch_down_gemm(bool fp8, const void* h, const void* w2, const float* s2,
+hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void* w13,
+                               const float* s13, const int32_t* sorted_ids,
+                               const int32_t* tile_seg, const int32_t* tile_row0,
+                               const int32_t* n_tiles, const int32_t* seg_off,
+                               const int32_t* seg_cnt, void* h, int H, int I, int k,
+                               int max_tiles, hipStream_t s);
+hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2, const float* s2,
                             const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
                             const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
@@ -67,12 +78,19 @@ hipError_t launch_down_gemm(bool fp8, const void* h, const void* w2, const float
 // with no valid row are skipped (their partials are never read).
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s);
-// y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows).
-hipError_t launch_down(int wkind, const void* h, const void* w2, const float* s2,
+// y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows; bf16 h in the
+// layout launch_gate_up writes).  packed: weights from launch_pack_weights.
+hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
                        int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
                        int bm, int max_rows, hipStream_t s);
+// Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
+// K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
+// s) of 512 elements at (t K/32 + s) 512, lane 16 g + m holding row 16 t + m,
+// columns 32 s + 8 g .. + 7.  `packed` kernels read this layout.
+hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t rows, int K,
+                               hipStream_t s);
 // out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), rounded once.
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,

@@ -6,8 +6,9 @@ from typing import Optional
 
 import torch
 
-from .binding import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, alloc_workspace, make_desc,
-                      moe_forward, moe_route)
+from .binding import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_LAYOUT_FRAG16,
+                      MOE_LAYOUT_ROW_MAJOR, alloc_workspace, make_desc, moe_forward,
+                      moe_pack_weights, moe_route)
 
 _ACT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _W = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_FP8_E4M3}
@@ -18,11 +19,13 @@ class DeviceLayer:
 
     router [E, H], w13 [E+ns, 2I, H], w2 [E+ns, H, I] (uint8 = fp8 e4m3fn codes
     with fp32 block scales s13 [E+ns, 2I/128, H/128], s2 [E+ns, H/128, I/128]).
+    packed=True re-lays the expert weights out once with moe_pack_weights and
+    keeps only that copy (bf16 / fp8 weights).
     """
 
     def __init__(self, router, w13, w2, topk: int, n_shared: int = 0,
                  s13: Optional[torch.Tensor] = None, s2: Optional[torch.Tensor] = None,
-                 device="cuda"):
+                 device="cuda", packed: bool = False):
         self.router = router.to(device).contiguous()
         self.w13 = w13.to(device).contiguous()
         self.w2 = w2.to(device).contiguous()
@@ -42,10 +45,14 @@ class DeviceLayer:
                 raise ValueError("fp8 weights need s2 [E+ns, H/128, I/128]")
         self.device = device
         self._ws = {}
+        self.layout = MOE_LAYOUT_ROW_MAJOR
+        if packed:
+            self.w13, self.w2 = moe_pack_weights(self.desc(1), self.w13, self.w2)
+            self.layout = MOE_LAYOUT_FRAG16
 
     def desc(self, T: int):
         return make_desc(T, self.H, self.E, self.I, self.n_shared, self.act, self.wd,
-                         self.s13, self.s2)
+                         self.s13, self.s2, w_layout=self.layout)
 
     def workspace(self, T: int) -> torch.Tensor:
         if T not in self._ws:

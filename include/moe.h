@@ -58,9 +58,12 @@ enum moe_status {
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
 
+/* Layout of w13 / w2 (see moe_pack_weights). */
+enum moe_weight_layout { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_FRAG16 = 1 };
+
 /* Layer descriptor (host struct).
  *   T         gathered rows, padding rows included (>= 1)
- *   H         hidden size (multiple of 64; of 128 with fp8 weights)
+ *   H         hidden size (multiple of 64; of 128 with bf16 activations)
  *   E         routed experts (1..256)
  *   n_shared  always-on shared experts, 0 or 1; stored after the routed
  *             experts at index E of w13 / w2; not covered by router_w
@@ -72,6 +75,9 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
  *   w13_scale fp8 only: fp32 [E+n_shared, 2I/128, H/128] block scales
  *   w2_scale  fp8 only: fp32 [E+n_shared, H/128, I/128] block scales
  *   block_m   GEMM block rows used inside moe_forward; 0 = library default
+ *   w_layout  MOE_LAYOUT_ROW_MAJOR: w13 / w2 as documented at moe_forward;
+ *             MOE_LAYOUT_FRAG16: the same weights re-laid out by
+ *             moe_pack_weights (BF16 activations only)
  */
 typedef struct moe_desc {
   int32_t T, H, E, n_shared, I;
@@ -79,6 +85,7 @@ typedef struct moe_desc {
   const float* w13_scale;
   const float* w2_scale;
   int32_t block_m;
+  int32_t w_layout;
 } moe_desc;
 
 /* Bytes of workspace moe_forward / moe_route need for this layer and topk
@@ -133,6 +140,24 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
                 const void* router_w, const void* w13, const void* w2,
                 int32_t topk, void* out, void* workspace,
                 size_t workspace_bytes, moe_stream_t stream);
+
+/* One-time re-layout of the expert weights (at load time) into the order in
+ * which the layer's MFMA kernels fetch them, so that each wave-wide weight
+ * load is one contiguous 1 KB (bf16) / 512 B (fp8) block instead of 16 rows x
+ * 64 B; moe_forward then takes desc->w_layout = MOE_LAYOUT_FRAG16.  Every
+ * 16-row x 32-column piece of a [rows, K] weight matrix (w13: rows = (E +
+ * n_shared) 2I, K = H; w2: rows = (E + n_shared) H, K = I) becomes a block of
+ * 512 elements at (t K/32 + s) 512 (t = row / 16, s = column / 32), whose
+ * element 8 (16 g + m) + i is W[16 t + m][32 s + 8 g + i].  The packed arrays
+ * have the sizes and dtypes of w13 / w2; block scales are unchanged.
+ *   desc        as for moe_forward (T, w_layout and the scale pointers are
+ *               not used); w_dtype BF16 or FP8_E4M3 with BF16 activations
+ *   w13, w2     row-major weights (read)
+ *   w13_packed, w2_packed  out, same sizes; must not alias the inputs
+ * Enqueued on `stream`; the caller keeps the packed arrays for the layer's
+ * lifetime.  Returns MOE_ERR_UNSUPPORTED for fp32 weights. */
+int moe_pack_weights(const moe_desc* desc, const void* w13, const void* w2,
+                     void* w13_packed, void* w2_packed, moe_stream_t stream);
 
 /* Message for a status code (host; static string). */
 const char* moe_status_str(int status);

@@ -30,11 +30,11 @@ def log(msg):
     sys.stdout.flush()
 
 
-def device_layer(inp, device="cuda"):
+def device_layer(inp, device="cuda", packed=False):
     from expert_layer_moe_amd import DeviceLayer
     cfg = inp.cfg
     return DeviceLayer(inp.router, inp.w13, inp.w2, cfg.k, cfg.n_shared,
-                       inp.s13, inp.s2, device=device)
+                       inp.s13, inp.s2, device=device, packed=packed)
 
 
 def run_gpu(inp, layer=None, x=None, valid=None):

@@ -40,7 +40,7 @@ def test_nm_shows_c_symbols():
 
 def _d(**kw):
     base = dict(T=256, H=7168, E=48, n_shared=0, I=640, act_dtype=moe.MOE_BF16,
-                w_dtype=moe.MOE_BF16, w13_scale=None, w2_scale=None, block_m=0)
+                w_dtype=moe.MOE_BF16, w13_scale=None, w2_scale=None, block_m=0, w_layout=0)
     base.update(kw)
     return moe_desc(**base)
 
@@ -65,6 +65,10 @@ def test_status_strings():
     (dict(w_dtype=moe.MOE_FP8_E4M3), 3, -1),     # fp8 without scales
     (dict(w_dtype=moe.MOE_FP8_E4M3, I=704, w13_scale=FAKE, w2_scale=FAKE), 3, -2),
     (dict(block_m=48), 3, -2),
+    (dict(w_layout=moe.MOE_LAYOUT_FRAG16), 3, 0),
+    (dict(w_layout=2), 3, -1),
+    (dict(w_layout=moe.MOE_LAYOUT_FRAG16, H=256, I=64, act_dtype=moe.MOE_F32,
+          w_dtype=moe.MOE_F32), 3, -2),
 ])
 def test_descriptor_validation(kw, topk, status):
     lib = moe.load_library()
@@ -103,6 +107,16 @@ def test_align_validation():
     assert lib.moe_align(ctypes.byref(d), None, 3, 32, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
+def test_pack_weights_validation():
+    lib = moe.load_library()
+    assert lib.moe_pack_weights(None, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_pack_weights(ctypes.byref(_d()), None, FAKE, FAKE, FAKE, None) == -1
+    assert lib.moe_pack_weights(ctypes.byref(_d()), FAKE, FAKE, FAKE, None, None) == -1
+    f32 = _d(H=256, I=64, act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32)
+    assert lib.moe_pack_weights(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert lib.moe_pack_weights(ctypes.byref(_d(I=650)), FAKE, FAKE, FAKE, FAKE, None) == -2
+
+
 def test_workspace_grows_with_batch():
     lib = moe.load_library()
     a = lib.moe_workspace_size(ctypes.byref(_d(T=128)), 3)
@@ -111,7 +125,7 @@ def test_workspace_grows_with_batch():
 
 
 def test_profile_hooks_without_records():
-    assert moe.stage_names() == ["route_logits", "route_topk", "align", "gate_up",
+    assert moe.stage_names() == ["route_logits", "route_topk", "align", "pack_x", "gate_up",
                                  "gate_up_gemm", "down", "down_gemm", "combine"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())

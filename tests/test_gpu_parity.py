@@ -134,13 +134,53 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("i", range(len(SMALL)))
-def test_small_layers_match_oracle(i):
+def test_small_layers_match_oracle(i, packed):
     kw = SMALL[i]
-    log(f"[case] small layer {i}: {kw}")
+    if packed and kw.get("w") == "f32":
+        pytest.skip("fp32 weights have no packed layout")
+    log(f"[case] small layer {i} packed={packed}: {kw}")
     inp = random_small(seed=100 + i, **kw)
-    gpu = run_gpu(inp)
+    gpu = run_gpu(inp, device_layer(inp, packed=packed))
     compare(inp, gpu)
+
+
+def _pack_reference(w: torch.Tensor) -> torch.Tensor:
+    """The documented fragment layout of a [rows, K] matrix, by reshaping:
+    (t, m, s, g, i) -> (t, s, g, m, i)."""
+    R, K = w.shape
+    return w.reshape(R // 16, 16, K // 32, 4, 8).permute(0, 2, 3, 1, 4).reshape(R, K)
+
+
+@pytest.mark.parametrize("w", ["bf16", "fp8"])
+def test_pack_weights_layout_bitwise(w):
+    import expert_layer_moe_amd as moe
+    inp = random_small(T=8, H=256, E=3, k=2, I=128, n_shared=1, w=w, seed=7)
+    ne, I, H = 4, 128, 256
+    d = moe.make_desc(8, H, 3, I, 1, moe.MOE_BF16,
+                      moe.MOE_BF16 if w == "bf16" else moe.MOE_FP8_E4M3)
+    w13, w2 = inp.w13.cuda(), inp.w2.cuda()
+    p13, p2 = moe.moe_pack_weights(d, w13, w2)
+    torch.cuda.synchronize()
+    as_int = (lambda t: t.view(torch.int16)) if w == "bf16" else (lambda t: t)
+    ref13 = _pack_reference(as_int(inp.w13).reshape(ne * 2 * I, H)).reshape(ne, 2 * I, H)
+    ref2 = _pack_reference(as_int(inp.w2).reshape(ne * H, I)).reshape(ne, H, I)
+    assert torch.equal(as_int(p13.cpu()), ref13)
+    assert torch.equal(as_int(p2.cpu()), ref2)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(T=300, H=1024, E=32, k=4, I=160, valid_frac=0.5),
+    dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
+    dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),
+])
+def test_packed_weights_give_identical_output(kw):
+    """Only the weight addresses change with the layout: same bits out."""
+    inp = random_small(seed=11, **kw)
+    a = run_gpu(inp, device_layer(inp, packed=False))
+    b = run_gpu(inp, device_layer(inp, packed=True))
+    assert np.array_equal(a["out"], b["out"])
 
 
 def test_all_rows_padding_gives_zero_output():
@@ -152,14 +192,16 @@ def test_all_rows_padding_gives_zero_output():
 
 
 # ------------------------------------------------------ full-size workloads --
-@pytest.mark.parametrize("name", ["tiny", "decode_e48", "decode_e256_shared",
-                                  "gather_padded_e48", "prefill_ub_fp8"])
-def test_workload_matches_oracle(name):
+# the benchmark runs the packed layout; decode_e48 is also checked row-major
+@pytest.mark.parametrize("name,packed", [
+    ("tiny", False), ("decode_e48", False), ("decode_e48", True),
+    ("decode_e256_shared", True), ("gather_padded_e48", True), ("prefill_ub_fp8", True)])
+def test_workload_matches_oracle(name, packed):
     cfg = get_config(name)
-    log(f"[case] {name}: generating inputs")
+    log(f"[case] {name} packed={packed}: generating inputs")
     inp = make_inputs(cfg)
     log(f"[case] {name}: GPU run")
-    gpu = run_gpu(inp)
+    gpu = run_gpu(inp, device_layer(inp, packed=packed))
     log(f"[case] {name}: oracle run")
     compare(inp, gpu)
 
@@ -181,7 +223,7 @@ def test_prefill_two_streams_match_unsplit_batch():
     the unsplit 16384-row batch; ub1 also matches the oracle."""
     cfg = get_config("prefill_ub_fp8")
     full = make_inputs(cfg.with_(T=16384, ub=None))
-    layer = device_layer(full)
+    layer = device_layer(full, packed=True)
     xd = full.x.cuda()
     ref = layer.forward(xd)
     s0, s1 = torch.cuda.Stream(), torch.cuda.Stream()
