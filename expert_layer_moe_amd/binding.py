@@ -22,7 +22,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
-           "moe_pack_weights", "moe_status_str", "moe_num_stages", "moe_stage_name",
+           "moe_pack_weights", "moe_set_path_thresholds", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
 
@@ -64,6 +64,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
     lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_set_path_thresholds.argtypes = [I32, I32]
+    lib.moe_set_path_thresholds.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_num_stages.argtypes = []
@@ -196,6 +198,12 @@ def moe_pack_weights(desc, w13, w2, w13_packed=None, w2_packed=None, stream=None
         _dev(w13_packed, "w13_packed", wd, (ne, 2 * I, H)),
         _dev(w2_packed, "w2_packed", wd, (ne, H, I)), _stream(stream)))
     return w13_packed, w2_packed
+
+
+def moe_set_path_thresholds(gemm_min_rows: int = 128, gemm_min_tiles: int = -1):
+    """Segments above gemm_min_rows rows use the tiled GEMM kernels once their
+    tiles number gemm_min_tiles (-1 = fill the chip).  Process-wide."""
+    _check(load_library().moe_set_path_thresholds(gemm_min_rows, gemm_min_tiles))
 
 
 def moe_status_str(status: int) -> str:

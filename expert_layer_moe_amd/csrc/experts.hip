@@ -111,8 +111,11 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restric
 // tokens, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
 // of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
 // grid.x = round_up(n_seg * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
+// bf16: three waves per SIMD (164 VGPRs, no spills) keep more weight loads in
+// flight; the fp8 variant keeps two (it would spill).
 template <int KS, int MT, int KU, bool FP8, bool PW>
-__global__ __launch_bounds__(256) void gate_up_stream_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 ? 2 : 3)))
+void gate_up_stream_kernel(
     const uint16_t* __restrict__ xp, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ h, int H, int I, int n_seg,

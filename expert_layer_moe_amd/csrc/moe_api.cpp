@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: validation, workspace layout, launch sequence.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <mutex>
 #include <vector>
@@ -35,6 +36,10 @@ struct Plan {
 // fragments reused across the tile) beat streaming the weights once per
 // 64-row pass.
 constexpr int kBigSegRows = 128;
+
+// Path thresholds (moe_set_path_thresholds); read when a call is planned.
+std::atomic<int> g_gemm_min_rows{kBigSegRows};
+std::atomic<int> g_gemm_min_tiles{-1};   // -1: enough tiles to fill the chip
 
 int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
@@ -95,15 +100,27 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->bm = kDefaultBM;
   p->ks = choose_ks(d);
   p->router_gemm = use_router_gemm(d);
+  const int min_rows = g_gemm_min_rows.load();
   p->big_thr = (d->act_dtype == MOE_BF16 && d->I % 128 == 0 && d->H <= moe::kMaxGemmK &&
                 d->I <= moe::kMaxGemmK)
-                   ? kBigSegRows
+                   ? min_rows
                    : INT_MAX;
   const size_t kk = (size_t)topk + p->ns;
   // the GEMM path only pays once its gate/up launch fills the chip
   // (256 blocks of I/128 columns each)
-  p->min_tiles = (256 + p->I / 128 - 1) / (p->I / 128 > 0 ? p->I / 128 : 1);
+  const int tiles_set = g_gemm_min_tiles.load();
+  p->min_tiles = tiles_set >= 0
+                     ? tiles_set
+                     : (256 + p->I / 128 - 1) / (p->I / 128 > 0 ? p->I / 128 : 1);
   p->max_tiles = (int)(((size_t)p->T * kk + 127) / 128 + p->E + p->ns);
+  // A segment holds at most T rows, and the 128-row tiles of the segments
+  // above big_thr rows number at most T kk / 128 + T kk / (big_thr + 1) + 1:
+  // when that cannot reach min_tiles the GEMM kernels would never run, so
+  // they are not launched.
+  if (p->big_thr != INT_MAX) {
+    const size_t bound = (size_t)p->T * kk / 128 + (size_t)p->T * kk / ((size_t)p->big_thr + 1) + 1;
+    if (p->T <= p->big_thr || bound < (size_t)p->min_tiles) p->big_thr = INT_MAX;
+  }
   p->cap = (int)round_up((size_t)p->T * kk + (size_t)(p->E + p->ns) * (p->bm - 1), p->bm);
   const size_t act_h = (p->act == MOE_F32) ? 4 : 2;
   size_t o = 0;
@@ -202,6 +219,13 @@ int moe_pack_weights(const moe_desc* desc, const void* w13, const void* w2, void
   if (moe::launch_pack_weights(wkind, w13, w13_packed, ne * 2 * d.I, d.H, s) != hipSuccess ||
       moe::launch_pack_weights(wkind, w2, w2_packed, ne * d.H, d.I, s) != hipSuccess)
     return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_set_path_thresholds(int32_t gemm_min_rows, int32_t gemm_min_tiles) {
+  if (gemm_min_rows < 0 || gemm_min_tiles < -1) return MOE_ERR_INVALID_ARG;
+  g_gemm_min_rows.store(gemm_min_rows);
+  g_gemm_min_tiles.store(gemm_min_tiles);
   return MOE_OK;
 }
 

@@ -159,6 +159,17 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
 int moe_pack_weights(const moe_desc* desc, const void* w13, const void* w2,
                      void* w13_packed, void* w2_packed, moe_stream_t stream);
 
+/* Path choice inside moe_forward (host; process-wide, read when a call
+ * starts).  Expert segments with more than gemm_min_rows rows go to the
+ * LDS-tiled GEMM kernels when their 128-row tiles number at least
+ * gemm_min_tiles (-1 = enough to fill the chip); all other segments stream
+ * the expert weights.  Defaults: 128, -1.  gemm_min_rows = INT32_MAX keeps
+ * every segment on the streaming kernels.  Both paths compute the same
+ * layer; this only moves work between kernels (tuning, and tests that cover
+ * both paths at small sizes).  Returns MOE_ERR_INVALID_ARG for
+ * gemm_min_rows < 0 or gemm_min_tiles < -1. */
+int moe_set_path_thresholds(int32_t gemm_min_rows, int32_t gemm_min_tiles);
+
 /* Message for a status code (host; static string). */
 const char* moe_status_str(int status);
 

@@ -11,6 +11,7 @@ valid rows within the tolerance of the weight dtype; padding rows exactly 0.
 from __future__ import annotations
 
 import sys
+import contextlib
 from dataclasses import dataclass
 
 import numpy as np
@@ -35,6 +36,18 @@ def device_layer(inp, device="cuda", packed=False):
     cfg = inp.cfg
     return DeviceLayer(inp.router, inp.w13, inp.w2, cfg.k, cfg.n_shared,
                        inp.s13, inp.s2, device=device, packed=packed)
+
+
+@contextlib.contextmanager
+def gemm_path(min_rows=16, min_tiles=1):
+    """Send segments above min_rows rows to the tiled GEMM kernels (at any
+    tile count) for the duration; restores the defaults."""
+    import expert_layer_moe_amd as moe
+    moe.moe_set_path_thresholds(min_rows, min_tiles)
+    try:
+        yield
+    finally:
+        moe.moe_set_path_thresholds()
 
 
 def run_gpu(inp, layer=None, x=None, valid=None):

@@ -117,6 +117,14 @@ def test_pack_weights_validation():
     assert lib.moe_pack_weights(ctypes.byref(_d(I=650)), FAKE, FAKE, FAKE, FAKE, None) == -2
 
 
+def test_path_thresholds_validation():
+    lib = moe.load_library()
+    assert lib.moe_set_path_thresholds(-1, -1) == -1
+    assert lib.moe_set_path_thresholds(16, -2) == -1
+    assert lib.moe_set_path_thresholds(16, 1) == 0
+    assert lib.moe_set_path_thresholds(128, -1) == 0
+
+
 def test_workspace_grows_with_batch():
     lib = moe.load_library()
     a = lib.moe_workspace_size(ctypes.byref(_d(T=128)), 3)

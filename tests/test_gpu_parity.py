@@ -1,5 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs.  Needs an MI355X."""
+import contextlib
+
 import numpy as np
 import pytest
 import torch
@@ -8,7 +10,7 @@ import oracle
 from workloads import get_config, make_inputs
 from workloads.gen import random_small
 
-from .parity import TOL, compare, device_layer, log, run_gpu
+from .parity import TOL, compare, device_layer, gemm_path, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -126,7 +128,7 @@ SMALL = [
     dict(T=1, H=128, E=4, k=1, I=32),
     dict(T=20, H=128, E=4, k=4, I=64),
     dict(T=300, H=1024, E=32, k=4, I=160, valid_frac=0.5),
-    # segments above 64 rows take the tiled GEMM kernels
+    # larger segments (with path "gemm" many of them take the tiled GEMMs)
     dict(T=300, H=256, E=4, k=2, I=128),
     dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
     dict(T=1100, H=256, E=16, k=2, I=64, valid_frac=0.7),   # + router GEMM
@@ -134,15 +136,29 @@ SMALL = [
 ]
 
 
+def _gemm_capable(kw):
+    return kw.get("act", "bf16") == "bf16" and kw["I"] % 128 == 0 and kw["H"] % 128 == 0
+
+
+@pytest.mark.parametrize("path", ["auto", "gemm"])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("i", range(len(SMALL)))
-def test_small_layers_match_oracle(i, packed):
+def test_small_layers_match_oracle(i, packed, path):
+    """path "gemm": segments above 16 rows take the tiled GEMM kernels (the
+    others stream), so both expert paths meet in one call."""
     kw = SMALL[i]
     if packed and kw.get("w") == "f32":
         pytest.skip("fp32 weights have no packed layout")
-    log(f"[case] small layer {i} packed={packed}: {kw}")
+    if path == "gemm" and not _gemm_capable(kw):
+        pytest.skip("shape outside the tiled GEMM kernels")
+    log(f"[case] small layer {i} packed={packed} path={path}: {kw}")
     inp = random_small(seed=100 + i, **kw)
-    gpu = run_gpu(inp, device_layer(inp, packed=packed))
+    layer = device_layer(inp, packed=packed)
+    if path == "gemm":
+        with gemm_path():
+            gpu = run_gpu(inp, layer)
+    else:
+        gpu = run_gpu(inp, layer)
     compare(inp, gpu)
 
 
@@ -175,11 +191,15 @@ def test_pack_weights_layout_bitwise(w):
     dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
     dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),
 ])
-def test_packed_weights_give_identical_output(kw):
+@pytest.mark.parametrize("path", ["auto", "gemm"])
+def test_packed_weights_give_identical_output(kw, path):
     """Only the weight addresses change with the layout: same bits out."""
+    if path == "gemm" and not _gemm_capable(kw):
+        pytest.skip("shape outside the tiled GEMM kernels")
     inp = random_small(seed=11, **kw)
-    a = run_gpu(inp, device_layer(inp, packed=False))
-    b = run_gpu(inp, device_layer(inp, packed=True))
+    with gemm_path() if path == "gemm" else contextlib.nullcontext():
+        a = run_gpu(inp, device_layer(inp, packed=False))
+        b = run_gpu(inp, device_layer(inp, packed=True))
     assert np.array_equal(a["out"], b["out"])
 
 
