@@ -7,8 +7,9 @@
 // Attention and TBO for DeepSeek-V4 on MI355X", PrefillDelayer section) carry
 // no assignment and are skipped.
 //
-// One 1024-thread workgroup: LDS histogram -> wave scan of the padded counts
-// -> stable scatter in 1024-assignment chunks.  Inside a chunk, a lane's rank
+// Small batches: one 1024-thread workgroup, LDS histogram -> wave scan of the
+// padded counts -> stable scatter in 1024-assignment chunks.  Large batches
+// split the same steps over spans of 4096 assignments (three launches).  Inside a chunk, a lane's rank
 // among the lanes of its wave with the same expert comes from nine ballots
 // over the bits of the expert id; ranks across the chunk's 16 waves come from
 // per-wave counts in LDS.  The result is unique and deterministic.
@@ -37,34 +38,13 @@ __device__ __forceinline__ int seg_of(const int32_t* ids, int a, int k, int kk,
   return (e0 >= 0 && e0 < E) ? E : -1;
 }
 
-__global__ __launch_bounds__(kAlignThreads) void align_kernel(
-    const int32_t* __restrict__ ids, int T, int k, int E, int ns, int bm,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
-    int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
-    int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
-    int32_t* __restrict__ n_tiles) {
-  __shared__ int cnt[kMaxSeg];
-  __shared__ int base[kMaxSeg];
-  __shared__ int wcnt[kAlignWaves][kMaxSeg];
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int nseg = E + ns;
-  const int kk = k + ns;
-  const int n_assign = T * kk;
-
-  for (int i = tid; i < kMaxSeg; i += kAlignThreads) cnt[i] = 0;
-  for (int i = tid; i < kAlignWaves * kMaxSeg; i += kAlignThreads)
-    (&wcnt[0][0])[i] = 0;
-  __syncthreads();
-
-  for (int a = tid; a < n_assign; a += kAlignThreads) {
-    const int e = seg_of(ids, a, k, kk, E);
-    if (e >= 0) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-
-  // Exclusive scan of the padded counts by wave 0 (5 segments per lane).
+// Exclusive scan of the padded segment counts (cnt in LDS) by wave 0 into
+// base (LDS) and offsets / n_post; wave 1 lists the 128-row tiles of the
+// segments above big_thr rows.  Ends with a barrier.
+__device__ void scan_segments(const int* cnt, int* base, int nseg, int bm, int32_t* offsets,
+                              int32_t* n_post, int big_thr, int min_tiles, int32_t* tile_seg,
+                              int32_t* tile_row0, int32_t* n_tiles) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   if (wave == 0) {
     int local[5];
     int sum = 0;
@@ -125,9 +105,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     if (lane == kWave - 1) *n_tiles = inc >= min_tiles ? inc : 0;
   }
   __syncthreads();
+}
 
-  // Sentinels at the tail of each segment, and the expert of each block.
-  for (int seg = tid; seg < nseg; seg += kAlignThreads) {
+// Sentinels at the tail of each segment, and the expert of each block.
+__device__ void pad_segments(const int* cnt, const int* base, int nseg, int bm,
+                             int32_t* sorted_ids, int32_t* block_expert, int32_t* seg_count) {
+  for (int seg = threadIdx.x; seg < nseg; seg += blockDim.x) {
     const int c = cnt[seg];
     if (seg_count) seg_count[seg] = c;
     const int p = (c + bm - 1) / bm * bm;
@@ -135,12 +118,19 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     for (int i = c; i < p; ++i) sorted_ids[o + i] = -1;
     for (int b = 0; b < p / bm; ++b) block_expert[o / bm + b] = seg;
   }
+}
 
-  // Stable scatter, chunk by chunk in flat assignment order.
+// Stable scatter of the assignments [a0, a1), chunk by chunk in flat order;
+// base[seg] (LDS) is the next free position of each segment and advances.
+// wcnt must be zero on entry and is zero on exit.
+__device__ void scatter_range(const int32_t* ids, int a0, int a1, int k, int kk, int E,
+                              int nseg, int* base, int (*wcnt)[kMaxSeg], int32_t* sorted_ids,
+                              int32_t* slot_pos) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int chunk = 0; chunk < n_assign; chunk += kAlignThreads) {
+  for (int chunk = a0; chunk < a1; chunk += kAlignThreads) {
     const int a = chunk + tid;
-    const int e = a < n_assign ? seg_of(ids, a, k, kk, E) : -1;
+    const int e = a < a1 ? seg_of(ids, a, k, kk, E) : -1;
     const unsigned key = static_cast<unsigned>(e + 1);  // 0..257: 9 bits
     uint64_t same = ~0ull;
 #pragma unroll
@@ -173,16 +163,140 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
 }
 
+// One 1024-thread block for the whole list (small batches).
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int ns, int bm,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
+    int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
+    int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int cnt[kMaxSeg];
+  __shared__ int base[kMaxSeg];
+  __shared__ int wcnt[kAlignWaves][kMaxSeg];
+  const int tid = threadIdx.x;
+  const int nseg = E + ns;
+  const int kk = k + ns;
+  const int n_assign = T * kk;
+
+  for (int i = tid; i < kMaxSeg; i += kAlignThreads) cnt[i] = 0;
+  for (int i = tid; i < kAlignWaves * kMaxSeg; i += kAlignThreads)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+
+  for (int a = tid; a < n_assign; a += kAlignThreads) {
+    const int e = seg_of(ids, a, k, kk, E);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  scan_segments(cnt, base, nseg, bm, offsets, n_post, big_thr, min_tiles, tile_seg, tile_row0,
+                n_tiles);
+  pad_segments(cnt, base, nseg, bm, sorted_ids, block_expert, seg_count);
+  scatter_range(ids, 0, n_assign, k, kk, E, nseg, base, wcnt, sorted_ids, slot_pos);
+}
+
+// Large batches, three launches over kAlignSpan-assignment spans:
+// 1. per-span segment counts -> span_cnt[span][seg];
+// 2. one block: totals, the scan, tiles, sentinels, and each span's start
+//    inside each segment -> span_cnt[span][seg] (overwritten);
+// 3. per span: the stable scatter from those starts.
+// Spans are in flat assignment order, so the result equals the one-block
+// kernel's.
+constexpr int kAlignSpan = 4 * kAlignThreads;
+
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int ns,
+    int32_t* __restrict__ span_cnt) {
+  __shared__ int cnt[kMaxSeg];
+  const int tid = threadIdx.x;
+  const int nseg = E + ns, kk = k + ns, n_assign = T * kk;
+  for (int i = tid; i < kMaxSeg; i += kAlignThreads) cnt[i] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kAlignSpan, a1 = min(n_assign, a0 + kAlignSpan);
+  for (int a = a0 + tid; a < a1; a += kAlignThreads) {
+    const int e = seg_of(ids, a, k, kk, E);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int seg = tid; seg < nseg; seg += kAlignThreads)
+    span_cnt[(size_t)blockIdx.x * nseg + seg] = cnt[seg];
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
+    int n_span, int E, int ns, int bm, int32_t* __restrict__ span_cnt,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
+    int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
+    int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
+    int32_t* __restrict__ n_tiles) {
+  __shared__ int cnt[kMaxSeg];
+  __shared__ int base[kMaxSeg];
+  const int tid = threadIdx.x;
+  const int nseg = E + ns;
+  for (int seg = tid; seg < nseg; seg += kAlignThreads) {
+    int c = 0;
+    for (int sp = 0; sp < n_span; ++sp) c += span_cnt[(size_t)sp * nseg + seg];
+    cnt[seg] = c;
+  }
+  __syncthreads();
+  scan_segments(cnt, base, nseg, bm, offsets, n_post, big_thr, min_tiles, tile_seg, tile_row0,
+                n_tiles);
+  pad_segments(cnt, base, nseg, bm, sorted_ids, block_expert, seg_count);
+  for (int seg = tid; seg < nseg; seg += kAlignThreads) {
+    int run = base[seg];
+    for (int sp = 0; sp < n_span; ++sp) {
+      const size_t i = (size_t)sp * nseg + seg;
+      const int c = span_cnt[i];
+      span_cnt[i] = run;
+      run += c;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int T, int k, int E, int ns,
+    const int32_t* __restrict__ span_start, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ slot_pos) {
+  __shared__ int base[kMaxSeg];
+  __shared__ int wcnt[kAlignWaves][kMaxSeg];
+  const int tid = threadIdx.x;
+  const int nseg = E + ns, kk = k + ns, n_assign = T * kk;
+  for (int seg = tid; seg < nseg; seg += kAlignThreads)
+    base[seg] = span_start[(size_t)blockIdx.x * nseg + seg];
+  for (int i = tid; i < kAlignWaves * kMaxSeg; i += kAlignThreads)
+    (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kAlignSpan, a1 = min(n_assign, a0 + kAlignSpan);
+  scatter_range(ids, a0, a1, k, kk, E, nseg, base, wcnt, sorted_ids, slot_pos);
+}
+
 }  // namespace
+
+int align_spans(int T, int k, int n_shared) {
+  const long long n = (long long)T * (k + n_shared);
+  return n > 2 * kAlignSpan ? (int)((n + kAlignSpan - 1) / kAlignSpan) : 0;
+}
 
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
                         int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
-                        int32_t* tile_row0, int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
-                     E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
-                     slot_pos, seg_count, big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
+                        int32_t* tile_row0, int32_t* n_tiles, int32_t* span_buf,
+                        hipStream_t s) {
+  const int n_span = align_spans(T, k, n_shared);
+  if (n_span == 0 || span_buf == nullptr) {
+    hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
+                       E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
+                       slot_pos, seg_count, big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(align_count_kernel, dim3(n_span), dim3(kAlignThreads), 0, s, ids, T, k, E,
+                     n_shared, span_buf);
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, n_span, E, n_shared,
+                     bm, span_buf, sorted_ids, block_expert, offsets, n_post, seg_count,
+                     big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(n_span), dim3(kAlignThreads), 0, s, ids, T, k,
+                     E, n_shared, span_buf, sorted_ids, slot_pos);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ struct Plan {
   int max_tiles;  // bound on their 128-row tiles
   int min_tiles;  // fewer tiles than this stay on the streaming kernels
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
-      off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_h, off_y, total;
+      off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_span, off_h, off_y, total;
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -137,6 +137,7 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_tseg = take((size_t)p->max_tiles * 4);
   p->off_trow = take((size_t)p->max_tiles * 4);
   p->off_ntiles = take(4);
+  p->off_span = take((size_t)moe::align_spans(p->T, p->k, p->ns) * (p->E + p->ns) * 4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
   // y (fp32 rows) also holds the packed token rows of the streaming gate/up
   // (cap x H bf16) until the down kernels overwrite it
@@ -271,7 +272,7 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
   if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
                         block_expert, expert_offsets, n_post_padded, nullptr, nullptr,
-                        INT_MAX, 0, nullptr, nullptr, nullptr,
+                        INT_MAX, 0, nullptr, nullptr, nullptr, nullptr,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -321,7 +322,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
     StageTimer tm(S_ALIGN, s);
     if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
                           slot, cnt, p.big_thr, p.min_tiles, gemm ? tseg : nullptr, trow,
-                          ntiles,
+                          ntiles, at<int32_t>(ws, p.off_span),
                           s) != hipSuccess)
       return MOE_ERR_HIP;
   }

@@ -28,11 +28,16 @@ hipError_t launch_route_topk(const float* part, int ks, const uint8_t* valid,
 // of every segment with more than big_thr rows, and their number; fewer
 // than min_tiles tiles (too few blocks to fill the chip) are dropped and
 // n_tiles is 0, leaving every segment to the streaming kernels.
+// Batches of more than 8192 assignments use align_spans(T, k, n_shared) spans
+// and need span_buf (that many x (E + n_shared) int32); with span_buf null
+// one block does the whole list.
+int align_spans(int T, int k, int n_shared);
 hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int bm, int32_t* sorted_ids, int32_t* block_expert,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
                         int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
-                        int32_t* tile_row0, int32_t* n_tiles, hipStream_t s);
+                        int32_t* tile_row0, int32_t* n_tiles, int32_t* span_buf,
+                        hipStream_t s);
 
 // ---- expert GEMMs ------------------------------------------------------------
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };

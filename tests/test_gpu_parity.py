@@ -133,6 +133,8 @@ SMALL = [
     dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
     dict(T=1100, H=256, E=16, k=2, I=64, valid_frac=0.7),   # + router GEMM
     dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),        # shared expert tiled
+    # more than 8192 assignments: the span-parallel align
+    dict(T=1200, H=256, E=64, k=8, I=128, n_shared=1, valid_frac=0.8),
 ]
 
 
