@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
   uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
   const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
   const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll 4
+#pragma unroll 8
   for (int s = s0 + wave; s < s1; s += 4)
     *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = sid >= 0 ? ld16(src + 32 * s) : zero;
 }
@@ -411,13 +411,12 @@ __global__ __launch_bounds__(256) void down_f32_kernel(
 // order, then the shared expert, rounded once.  Padding rows -> 0.
 constexpr int kMaxSlots = 17;
 
+template <int NV>
 __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ y, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
     int H, int k, int ns, void* __restrict__ out, int out_bf16) {
   const int t = blockIdx.x;
-  const int nbeg = blockIdx.y * blockDim.x * 4;
-  const int nend = min(H, nbeg + (int)blockDim.x * 4);
   const bool valid = ids[(size_t)t * k] >= 0;
   const int kk = k + ns;
   int pos[kMaxSlots];
@@ -427,26 +426,41 @@ __global__ __launch_bounds__(256) void combine_kernel(
     pos[j] = (valid && j < kk) ? slot_pos[(size_t)t * kk + j] : 0;
     wt[j] = (valid && j < k) ? w[(size_t)t * k + j] : 1.f;
   }
-  for (int n = nbeg + threadIdx.x * 4; n < nend; n += blockDim.x * 4) {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
+  // NV groups of 4 columns per thread, each group coalesced across the block;
+  // all loads of a thread are issued before the sums
+  int n[NV];
+  floatx4 acc[NV];
 #pragma unroll
-      for (int j = 0; j < kMaxSlots; ++j) {
-        if (j < kk) {
-          const floatx4 v = *reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n);
+  for (int v = 0; v < NV; ++v) {
+    n[v] = ((blockIdx.y * NV + v) * 256 + threadIdx.x) * 4;
+    acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (valid) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = fmaf(wt[j], v[i], acc[i]);
+    for (int j = 0; j < kMaxSlots; ++j) {
+      if (j < kk) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+          if (n[v] < H) {
+            const floatx4 val = *reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
+          }
         }
       }
     }
+  }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (n[v] >= H) continue;
     if (out_bf16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)t * H + n;
+      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)t * H + n[v];
       u32x2 pk;
-      pk[0] = (uint32_t)f32_to_bf16_bits(acc[0]) | ((uint32_t)f32_to_bf16_bits(acc[1]) << 16);
-      pk[1] = (uint32_t)f32_to_bf16_bits(acc[2]) | ((uint32_t)f32_to_bf16_bits(acc[3]) << 16);
+      pk[0] = (uint32_t)f32_to_bf16_bits(acc[v][0]) | ((uint32_t)f32_to_bf16_bits(acc[v][1]) << 16);
+      pk[1] = (uint32_t)f32_to_bf16_bits(acc[v][2]) | ((uint32_t)f32_to_bf16_bits(acc[v][3]) << 16);
       *reinterpret_cast<u32x2*>(o) = pk;
     } else {
-      *reinterpret_cast<floatx4*>(static_cast<float*>(out) + (size_t)t * H + n) = acc;
+      *reinterpret_cast<floatx4*>(static_cast<float*>(out) + (size_t)t * H + n[v]) = acc[v];
     }
   }
 }
@@ -619,8 +633,13 @@ hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, y, ids, w, slot_pos,
-                     T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  // two 4-column groups per thread once there are rows enough to fill the chip
+  if (T >= 256)
+    hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, y, ids,
+                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, y, ids,
+                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
