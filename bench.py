@@ -32,13 +32,14 @@ CSRC = os.path.join(ROOT, "expert_layer_moe_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-# sources that define the expert GEMM kernels (counter records name this hash)
-KERNEL_SOURCES = ("experts.hip", "moe_common.h")
+# sources that define each timed kernel (counter records name this hash)
+KERNEL_SOURCES = {"gate_up": ("experts.hip", "moe_common.h"),
+                  "gate_up_gemm": ("gemm.hip", "moe_common.h")}
 
 
-def source_sha() -> str:
+def source_sha(kernel: str = "gate_up") -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -77,7 +78,7 @@ def algorithmic_work(cfg, ids, n_valid):
     )
 
 
-def cpu_baseline(inp, budget_s=12.0):
+def cpu_baseline(inp, min_s=10.0, max_s=30.0):
     """The oracle, as it stands, on the host cores (bounded sample)."""
     import oracle
     from threadpoolctl import threadpool_info
@@ -93,13 +94,15 @@ def cpu_baseline(inp, budget_s=12.0):
                              router=inp.router, w13=inp.w13, w2=inp.w2,
                              s13=inp.s13, s2=inp.s2)
         desc = f"first {n} rows of the {cfg.name} batch ({sample.n_valid} valid)"
+    # repeated runs for about 10-30 s of host work (at least 3 runs)
     times = []
-    t_end = time.time() + budget_s
+    start = time.time()
     while True:
         t0 = time.perf_counter()
         oracle.moe_forward(sample)
         times.append(time.perf_counter() - t0)
-        if time.time() > t_end or len(times) >= 5:
+        spent = time.time() - start
+        if (spent >= min_s and len(times) >= 3) or spent + times[-1] > max_s:
             break
     t = sorted(times)[len(times) // 2]
     return {"value": round(sample.n_valid / t, 2), "unit": "tokens/s",
@@ -114,7 +117,7 @@ def traffic_for(kernel: str, workload: str):
             rec = json.load(f).get(f"{kernel}:{workload}")
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_sha():
+    if not rec or rec.get("source_sha") != source_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -278,7 +281,7 @@ def run(args):
         "touched_experts": work["touched_experts"],
         "ms_per_step_without_events": round(ms_clean / args.steps, 5),
     }
-    res["source_sha"] = source_sha()
+    res["source_sha"] = source_sha(dom if not pair else "gate_up_gemm")
     if args.cpu_baseline and not pair:
         log("[bench] timing the CPU oracle")
         res["cpu_baseline"] = cpu_baseline(inp)

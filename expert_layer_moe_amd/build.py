@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoe_amd.so")
 
-SOURCES = ["route.hip", "align.hip", "experts.hip", "gemm.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "align.hip", "layout.hip", "experts.hip", "gemm.hip", "moe_api.cpp"]
 HEADERS = ["moe_common.h", "moe_kernels.h"]
 
 HIPCC_FLAGS = [

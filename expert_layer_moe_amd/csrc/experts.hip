@@ -1,11 +1,11 @@
-// Expert grouped GEMMs and the weighted combine.
+// Weight-streaming expert grouped GEMMs (the decode regime, bound by HBM).
 //
 // gate/up: h = SiLU(W_gate x) * (W_up x) per sorted row (the expert MLP of a
 // sparse MoE layer, "AMD Instinct MI355X: ATOM ...": sparse MoE experts,
 // block-scale GEMMs); down: y = W2 h ("[SGLang] Single Batch Overlap for MoE
-// models": the down-projection GEMM); combine: out[t] = sum_j w[t,j] y(t,j)
-// plus the always-on shared expert ("Step3 Inference Optimization on AMD
-// Instinct MI308X", optimisation list: shared-expert MLP fused in the layer).
+// models": the down-projection GEMM).  The shared expert of "Step3 Inference
+// Optimization on AMD Instinct MI308X" (optimisation list) is one more
+// segment.
 //
 // fp8 weights (same list: FP8 blockscale) are OCP e4m3fn codes with one fp32
 // scale per 128x128 block; codes become bf16 exactly, MFMA accumulates each
@@ -16,13 +16,6 @@
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ u32x2 ld8(const void* p) {
-  return *reinterpret_cast<const u32x2*>(p);
-}
 
 template <bool FP8>
 __device__ __forceinline__ bf16x8 load_w8(const void* base, size_t elem_off) {
@@ -39,67 +32,6 @@ __device__ __forceinline__ bf16x8 load_w8(const void* base, size_t elem_off) {
 // token rows) share that XCD's L2.  nb must be a multiple of 8.
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
-}
-
-// ---------------------------------------------------------------------------
-// Token rows of the streaming kernels in MFMA A-fragment order.  For a matrix
-// of K columns split in 16-row tiles, tile t occupies 16 K elements: K/32
-// steps of 64 lanes x 8 elements, lane 16 g + m holding row 16 t + m,
-// columns 32 s + 8 g .. + 7 of step s.  A wave then fetches a whole
-// fragment as 1 KB contiguous instead of 16 rows x 64 B, which leaves more of
-// the memory system to the weight stream.  The down projection's input h is
-// written in the same order.
-__device__ __forceinline__ size_t frag_index(int row, int col, int K) {
-  return (size_t)(row >> 4) * 16 * K + (size_t)((col >> 5) * 64 + ((col >> 3) & 3) * 16 + (row & 15)) * 8 +
-         (col & 7);
-}
-
-// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15 (padding rows 0),
-// for the tiles of segments left to the streaming kernels.
-// grid = (cap / 16, chunks of kpc steps).
-__global__ __launch_bounds__(256) void pack_x_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ n_post,
-    const int32_t* __restrict__ seg_cnt, int big_thr, const int32_t* __restrict__ gemm_tiles,
-    uint16_t* __restrict__ xp, int H, int k, int kpc) {
-  const int tile = blockIdx.x;
-  if (tile * 16 >= *n_post) return;
-  const int cnt = seg_cnt[block_expert[tile]];
-  if (cnt > big_thr && *gemm_tiles > 0) return;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int m = lane % 16, g = lane / 16;
-  const int sid = sorted_ids[tile * 16 + m];
-  const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
-  uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
-  const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll 8
-  for (int s = s0 + wave; s < s1; s += 4)
-    *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = sid >= 0 ? ld16(src + 32 * s) : zero;
-}
-
-// Weights in MFMA B-fragment order (the same tile / step / lane order as
-// frag_index, over a [rows, K] matrix): block (16-row tile t, K step s) of
-// 512 elements at (t * K/32 + s) * 512, lane 16 g + m holding row 16 t + m,
-// columns 32 s + 8 g .. + 7.  One thread moves one lane's 8 elements
-// (ESZ bytes each).
-template <int ESZ>
-__global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restrict__ src,
-                                                        uint8_t* __restrict__ dst,
-                                                        size_t n_lanes, int K) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_lanes) return;
-  const int lane = (int)(i & 63);
-  const size_t blk = i >> 6;
-  const size_t steps = (size_t)K / 32;
-  const size_t t = blk / steps, st = blk - t * steps;
-  const size_t row = t * 16 + (lane & 15);
-  const size_t col = st * 32 + 8 * (lane >> 4);
-  const uint8_t* p = src + (row * K + col) * ESZ;
-  if constexpr (ESZ == 2)
-    *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(p);
-  else
-    *reinterpret_cast<u32x2*>(dst + i * 8) = *reinterpret_cast<const u32x2*>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -407,64 +339,6 @@ __global__ __launch_bounds__(256) void down_f32_kernel(
   }
 }
 
-// Combine: one block per token row; fp32 sum over the k routed slots in slot
-// order, then the shared expert, rounded once.  Padding rows -> 0.
-constexpr int kMaxSlots = 17;
-
-template <int NV>
-__global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ y, const int32_t* __restrict__ ids,
-    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
-    int H, int k, int ns, void* __restrict__ out, int out_bf16) {
-  const int t = blockIdx.x;
-  const bool valid = ids[(size_t)t * k] >= 0;
-  const int kk = k + ns;
-  int pos[kMaxSlots];
-  float wt[kMaxSlots];
-#pragma unroll
-  for (int j = 0; j < kMaxSlots; ++j) {
-    pos[j] = (valid && j < kk) ? slot_pos[(size_t)t * kk + j] : 0;
-    wt[j] = (valid && j < k) ? w[(size_t)t * k + j] : 1.f;
-  }
-  // NV groups of 4 columns per thread, each group coalesced across the block;
-  // all loads of a thread are issued before the sums
-  int n[NV];
-  floatx4 acc[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    n[v] = ((blockIdx.y * NV + v) * 256 + threadIdx.x) * 4;
-    acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (valid) {
-#pragma unroll
-    for (int j = 0; j < kMaxSlots; ++j) {
-      if (j < kk) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          if (n[v] < H) {
-            const floatx4 val = *reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    if (n[v] >= H) continue;
-    if (out_bf16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + (size_t)t * H + n[v];
-      u32x2 pk;
-      pk[0] = (uint32_t)f32_to_bf16_bits(acc[v][0]) | ((uint32_t)f32_to_bf16_bits(acc[v][1]) << 16);
-      pk[1] = (uint32_t)f32_to_bf16_bits(acc[v][2]) | ((uint32_t)f32_to_bf16_bits(acc[v][3]) << 16);
-      *reinterpret_cast<u32x2*>(o) = pk;
-    } else {
-      *reinterpret_cast<floatx4*>(static_cast<float*>(out) + (size_t)t * H + n[v]) = acc[v];
-    }
-  }
-}
-
 }  // namespace
 
 namespace {
@@ -542,18 +416,6 @@ int round8(int v) { return (v + 7) / 8 * 8; }
 
 }  // namespace
 
-hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
-                         const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
-                         const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
-                         int max_rows, hipStream_t s) {
-  if (bm != 16 || H % 32 != 0) return hipErrorInvalidValue;
-  const int kpc = 32;   // MFMA steps per block
-  hipLaunchKernelGGL(pack_x_kernel, dim3(max_rows / 16, (H / 32 + kpc - 1) / kpc), dim3(256), 0,
-                     s, static_cast<const uint16_t*>(x), sorted_ids, block_expert, n_post,
-                     seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc);
-  return hipGetLastError();
-}
-
 hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
@@ -611,35 +473,6 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
     if (packed) launch_dn_ku<false, true>(ku, a);
     else launch_dn_ku<false, false>(ku, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t rows, int K,
-                               hipStream_t s) {
-  if (wkind == W_F32 || rows % 16 != 0 || K % 32 != 0) return hipErrorInvalidValue;
-  const size_t n_lanes = rows * (size_t)K / 8;
-  const size_t blocks = (n_lanes + 255) / 256;
-  if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
-  if (wkind == W_BF16)
-    hipLaunchKernelGGL(pack_frag_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), n_lanes, K);
-  else
-    hipLaunchKernelGGL(pack_frag_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), n_lanes, K);
-  return hipGetLastError();
-}
-
-hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
-                          const int32_t* slot_pos, int T, int H, int k,
-                          int n_shared, void* out, bool out_bf16,
-                          hipStream_t s) {
-  // two 4-column groups per thread once there are rows enough to fill the chip
-  if (T >= 256)
-    hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, y, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
-  else
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, y, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 

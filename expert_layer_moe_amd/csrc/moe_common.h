@@ -56,4 +56,20 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return __fdividef(g, 1.0f + __expf(-g)) * u;
 }
 
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const void* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// MFMA fragment order of a [rows, K] bf16 matrix in 16-row tiles: tile t
+// holds K/32 steps of 64 lanes x 8 elements, lane 16 g + m carrying row
+// 16 t + m, columns 32 s + 8 g .. + 7 of step s.  A wave then fetches a whole
+// fragment as 1 KB contiguous instead of 16 rows x 64 B.
+__device__ __forceinline__ size_t frag_index(int row, int col, int K) {
+  return (size_t)(row >> 4) * 16 * K + (size_t)((col >> 5) * 64 + ((col >> 3) & 3) * 16 + (row & 15)) * 8 +
+         (col & 7);
+}
+
 }  // namespace moe
