@@ -328,6 +328,115 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     }
 }
 
+// 8 fp8 codes (two dwords) -> 8 bf16 of value(q) * s, rounded to nearest even
+__device__ __forceinline__ bf16x8 fp8x8_scaled(u32x2 v, float s) {
+  uint32_t out[4];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(v[w], true);
+    out[2 * w] = pack_bf16x2(f01[0] * s, f01[1] * s);
+    out[2 * w + 1] = pack_bf16x2(f23[0] * s, f23[1] * s);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{out[0], out[1], out[2], out[3]});
+}
+
+// Down projection of the large segments for K = I = 32 KSTEPS (128 or 256):
+// a block keeps the h rows of one 128-row tile in LDS (MFMA fragment order,
+// loaded once) and sweeps a chunk of output columns.  Each wave takes 64
+// output columns at a time: their W2 fragments (the MFMA A operand, straight
+// from global memory; fp8 dequantised in registers as bf16(q s)) against the
+// resident h fragments (the B operand), so a lane ends with 4 consecutive
+// output columns of one row and stores them as 16 bytes.
+// grid.x = round_up(max_tiles * n_chunks, 8); chunk = 256 * CPW columns.
+constexpr int kTallCPW = 4;   // 64-column tiles per wave per chunk
+
+template <int KSTEPS, bool FP8, bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void down_tall_kernel(
+    const uint16_t* __restrict__ h, const void* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int n_chunks,
+    int max_tiles) {
+  constexpr int I = 32 * KSTEPS;
+  __shared__ u32x4 hbuf[8 * KSTEPS][kWave];   // (row tile, step) slots, 1 KB each
+  const int lid = xcd_remap_g(blockIdx.x, gridDim.x);
+  if (lid >= max_tiles * n_chunks) return;
+  const int mt_id = lid / n_chunks, ch = lid - mt_id * n_chunks;
+  if (mt_id >= *n_tiles_ptr) return;
+  const int e = tile_seg[mt_id];
+  const int r0 = tile_row0[mt_id];
+  const int row_base = seg_off[e] + r0;
+  const int rows_here = min(kBM, seg_cnt[e] - r0);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int m = lane % 16, g = lane / 16;
+
+  // h tile -> LDS: piece P = (row, 8-element piece kp); K = 8 kp = 32 s + 8 gg
+#pragma unroll
+  for (int i = 0; i < 128 * I / 8 / 256; ++i) {
+    const int P = i * 256 + tid;
+    const int row = P / (I / 8), kp = P - row * (I / 8);
+    const int rr = min(row, rows_here - 1);
+    const u32x4 v = ld16(h + (size_t)(row_base + rr) * I + 8 * kp);
+    const int st = kp >> 2, gg = kp & 3;
+    hbuf[(row >> 4) * KSTEPS + st][swz(gg * 16 + (row & 15), st & 1)] = v;
+  }
+  // fp8: the W2 block scales of this expert ([H/128][I/128])
+  const float* sc = FP8 ? s2 + (size_t)e * (H / 128) * (I / 128) : nullptr;
+  const size_t wexp = (size_t)e * H * I;   // first element of expert e's W2
+  __syncthreads();
+
+  const int c_beg = ch * 256 * kTallCPW;
+  // W2 element offset of this lane's fragment of 16-column group n at step st
+  auto woff = [&](int n, int st) -> size_t {
+    if constexpr (PW) return wexp + ((size_t)(n / 16) * KSTEPS + st) * 512 + 8 * lane;
+    else return wexp + (size_t)(n + m) * I + 32 * st + 8 * g;
+  };
+  auto tile_n0 = [&](int t) { return c_beg + (t * 4 + wave) * 64; };
+  for (int t = 0; t < kTallCPW; ++t) {
+    const int n0 = tile_n0(t);
+    if (n0 >= H) break;
+    float sk[KSTEPS / 4];   // fp8: scales of the tile's 128-row block, per 128-wide K block
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kb = 0; kb < KSTEPS / 4; ++kb) sk[kb] = sc[(n0 / 128) * (I / 128) + kb];
+    }
+    floatx4 acc[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st) {
+      bf16x8 wa[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (FP8)
+          wa[q] = fp8x8_scaled(ld8(static_cast<const uint8_t*>(w2) + woff(n0 + 16 * q, st)),
+                               sk[st / 4]);
+        else
+          wa[q] = as_bf16x8(ld16(static_cast<const uint16_t*>(w2) + woff(n0 + 16 * q, st)));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
+      }
+    }
+    // acc[q][mt] lane (m, g) element i: output column n0 + 16 q + 4 g + i of
+    // tile row mt * 16 + m (16-byte stores; H is a multiple of 64)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int row = mt * 16 + m;
+      if (row >= rows_here) continue;
+      float* yr = y + (size_t)(row_base + row) * H;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *reinterpret_cast<floatx4*>(yr + n0 + 16 * q + 4 * g) = acc[q][mt];
+    }
+  }
+}
+
 int round8g(int v) { return (v + 7) / 8 * 8; }
 
 template <int OP, bool FP8, bool PW>
@@ -380,6 +489,23 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
                             const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
                             hipStream_t s) {
   if (I % 128 != 0 || I > kMaxGemmK) return hipErrorInvalidValue;
+  if (I == 128 || I == 256) {
+    const int n_chunks = (H + 256 * kTallCPW - 1) / (256 * kTallCPW);
+    const dim3 grid(round8g(max_tiles * n_chunks));
+    const uint16_t* hb = static_cast<const uint16_t*>(h);
+#define MOE_TALL(KS, F8, P)                                                                 \
+  hipLaunchKernelGGL((down_tall_kernel<KS, F8, P>), grid, dim3(256), 0, s, hb, w2, s2,      \
+                     tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, y, H, n_chunks, max_tiles)
+    if (I == 128) {
+      if (fp8) { if (packed) MOE_TALL(4, true, true); else MOE_TALL(4, true, false); }
+      else { if (packed) MOE_TALL(4, false, true); else MOE_TALL(4, false, false); }
+    } else {
+      if (fp8) { if (packed) MOE_TALL(8, true, true); else MOE_TALL(8, true, false); }
+      else { if (packed) MOE_TALL(8, false, true); else MOE_TALL(8, false, false); }
+    }
+#undef MOE_TALL
+    return hipGetLastError();
+  }
   const int n_nt = (H + kBN - 1) / kBN;
   launch_gemm_w<OP_DOWN>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
                          static_cast<const uint16_t*>(h), w2, s2, nullptr, tile_seg, tile_row0,
