@@ -263,3 +263,33 @@ def test_prefill_two_streams_match_unsplit_batch():
     ids, w, lg = layer.route(ub1.x.cuda(), None, logits=True)
     gpu.update(ids=ids.cpu().numpy(), w=w.cpu().double().numpy())
     compare(ub1, gpu)
+
+
+# ---------------------------------------------------------- graph capture --
+@pytest.mark.parametrize("kw,path", [
+    (dict(T=256, H=512, E=16, k=3, I=128, valid_frac=0.9), "auto"),
+    (dict(T=300, H=256, E=4, k=2, I=128, w="fp8", n_shared=1), "gemm"),
+])
+def test_forward_replays_in_a_hip_graph(kw, path):
+    """moe_forward only enqueues kernels (no allocation, memset or sync), so it
+    captures into a HIP graph; every replay, with eager work and
+    synchronisations between replays, matches the eager call bit for bit."""
+    inp = random_small(seed=21, **kw)
+    layer = device_layer(inp, packed=True)
+    xd = inp.x.cuda()
+    vd = None if inp.valid is None else inp.valid.cuda()
+    with gemm_path() if path == "gemm" else contextlib.nullcontext():
+        ref = layer.forward(xd, vd)
+        out = torch.empty_like(ref)
+        ws = layer.workspace(xd.shape[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(xd, vd, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        assert torch.isfinite(junk)
