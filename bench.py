@@ -159,12 +159,11 @@ def run(args):
         out1 = torch.empty_like(x1)
         ws1 = torch.empty_like(ws)
         streams = (torch.cuda.Stream(), torch.cuda.Stream())
-    cur = torch.cuda.current_stream()
-
     def step():
         if not pair:
             layer.forward(x, valid, out, ws)
             return
+        cur = torch.cuda.current_stream()
         ev = torch.cuda.Event()
         ev.record(cur)
         for s, xx, oo, ww in ((streams[0], x, out, ws), (streams[1], x1, out1, ws1)):
@@ -234,6 +233,26 @@ def run(args):
     torch.cuda.synchronize()
     ms_clean = c0.elapsed_time(c1)
 
+    # HIP-graph pass: the step (both streams for the pair) captured once and
+    # replayed K times; moe_forward only enqueues kernels, so it captures
+    graph = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_g = g0.elapsed_time(g1) / args.steps
+        graph = {"ms_per_step": round(ms_g, 5),
+                 "tokens_per_s": round(n_valid * (2 if pair else 1) / (ms_g / 1e3), 1)}
+
     ms_step = ms_total / args.steps
     tokens_per_step = n_valid * (2 if pair else 1)
     value = tokens_per_step / (ms_step / 1e3)
@@ -281,6 +300,7 @@ def run(args):
         "touched_experts": work["touched_experts"],
         "ms_per_step_without_events": round(ms_clean / args.steps, 5),
     }
+    res["graph_replay"] = graph
     res["source_sha"] = source_sha(dom if not pair else "gate_up_gemm")
     if args.cpu_baseline and not pair:
         log("[bench] timing the CPU oracle")
@@ -298,6 +318,8 @@ def main():
     ap.add_argument("--config", default="decode_e48")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay pass")
     ap.add_argument("--row-major", action="store_true",
                     help="time the expert weights in the row-major layout they are handed over in")
     args = ap.parse_args()

@@ -293,3 +293,41 @@ def test_forward_replays_in_a_hip_graph(kw, path):
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
         assert torch.isfinite(junk)
+
+
+def test_two_stream_pair_replays_in_a_hip_graph():
+    """The ub0/ub1 pair on two HIP streams (forked and joined with events)
+    captures into one graph; replays match the eager pair bit for bit."""
+    inp = random_small(T=512, H=256, E=8, k=2, I=128, w="fp8", seed=23)
+    layer = device_layer(inp, packed=True)
+    xd = inp.x.cuda()
+    halves = (xd[:256], xd[256:])
+    wss = (layer.workspace(256), torch.empty_like(layer.workspace(256)))
+    outs = [torch.empty_like(h) for h in halves]
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+
+    def pair():
+        cur = torch.cuda.current_stream()
+        ev = torch.cuda.Event()
+        ev.record(cur)
+        for s, xx, oo, ww in zip(streams, halves, outs, wss):
+            s.wait_event(ev)
+            with torch.cuda.stream(s):
+                layer.forward(xx, None, oo, ww, stream=s)
+        for s in streams:
+            cur.wait_stream(s)
+
+    pair()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    assert torch.equal(torch.cat(ref), layer.forward(xd))   # = the unsplit batch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pair()
+    for i in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref)), f"replay {i}"
