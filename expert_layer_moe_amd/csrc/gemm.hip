@@ -1,27 +1,25 @@
 // LDS-tiled MFMA GEMMs for expert segments of many rows (the prefill regime,
 // bound by MFMA issue rather than by HBM), and for the router of large
-// batches.
+// batches.  Prefill is compute-bound ("Step3 Inference Optimization on AMD
+// Instinct MI308X", results: prefill favours the part with more compute), so
+// a block works on a 128-row tile of one expert's sorted rows; fp8 weights
+// ("AMD Instinct MI355X: ATOM ...": block-scale GEMM; Step3 page: FP8
+// blockscale) are dequantised as value(q) * s in fp32 rounded to bf16.
 //
-// Prefill is compute-bound ("Step3 Inference Optimization on AMD Instinct
-// MI308X", results: prefill favours the part with more compute), so a block
-// works on a 128-row tile of one expert's rows against 256 weight rows:
-//   gate/up: 128 intermediate columns (128 gate rows + the matching 128 up
-//            rows of W13), epilogue h = SiLU(g) * u;
-//   down:    256 output columns (rows of W2), epilogue y (fp32);
-//   router:  256 experts (rows of R), epilogue logits (fp32).
-// 4 waves in a 2 x 2 grid; a wave owns 64 rows x 8 weight tiles of 16 rows
-// (32 MFMA 16x16x32 tiles; gate/up waves hold 4 gate tiles and the 4 matching
-// up tiles so SiLU * u is formed in registers).
+//   gate_up_tall_kernel: 128 rows x (128 gate + 128 up columns); weights as
+//     the MFMA A operand straight from memory, x rows through LDS, epilogue
+//     h = SiLU(g) * u.
+//   down_tall_kernel (K = I <= 256): the 128 h rows resident in LDS, a sweep
+//     over output columns, weights as the A operand; y rows fp32.
+//   gemm_kernel (down for larger I, and the router): 128 rows x 256 weight
+//     rows, both operands staged through LDS per 64-wide K window.
 //
-// K runs in windows of 64.  Both operands of a window are staged through LDS
-// in MFMA fragment order: slot (16-row tile, step j) = 64 lanes x 16 B, lane
-// g*16 + r holding row r, K = 32 j + 8 g + (0..7) of the window.  Weights come
-// row-major or already in that order (fragment-packed, one contiguous 1 KB /
-// 512 B block per tile and step).  Global loads run two windows ahead in registers
-// (window w+2 in flight while w is multiplied and w+1 is written to LDS), and
-// two LDS buffers alternate.  fp8 weights ("AMD Instinct MI355X: ATOM ...":
-// block-scale GEMM; Step3 page: FP8 blockscale) are dequantised once per block
-// while staged: value(q) * s in fp32, rounded to bf16.
+// Fragment order everywhere: an LDS slot (16-row tile, step j) is 64 lanes x
+// 16 B, lane g*16 + r holding row r, K = 32 j + 8 g + (0..7) of the window.
+// Weights come row-major or already in that order (fragment-packed, one
+// contiguous 1 KB / 512 B block per tile and step).
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -39,7 +37,7 @@ __device__ __forceinline__ int xcd_remap_g(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
 }
 
-enum GemmOp { OP_GATE_UP = 0, OP_DOWN = 1, OP_ROUTER = 2 };
+enum GemmOp { OP_DOWN = 1, OP_ROUTER = 2 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -69,8 +67,10 @@ __device__ __forceinline__ void fp8x16_scaled(u32x4 v, float s, u32x4& lo, u32x4
 // groups, so neither side conflicts.
 __device__ __forceinline__ int swz(int l, int j) { return l ^ (((l >> 4) << 1) | j); }
 
-// OP_GATE_UP: A = x rows of the tile's tokens (K = H); weight row wr < 128 is
-//   gate column nt*128 + wr, wr >= 128 the up column I + nt*128 + wr - 128.
+// Both operands through LDS; a wave of the 2 x 2 grid owns 64 rows x 8
+// weight tiles of 16 rows (32 MFMA 16x16x32 tiles).  Register stages run two
+// windows ahead (window w+2 in flight while w is multiplied and w+1 is
+// written to LDS), and two LDS buffers alternate.
 // OP_DOWN: A = h rows (K = I); weight rows nt*256 + wr of W2.
 // OP_ROUTER: A = x rows (padding rows enter as zeros, never used); weight
 //   rows nt*256 + wr of R.
@@ -122,8 +122,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     const int row = (tid >> 3) + 32 * s;
     const int rr = min(row, rows_here - 1);
     size_t src_row;
-    if constexpr (OP == OP_GATE_UP) src_row = (size_t)(sorted_ids[row_base + rr] / k);
-    else src_row = (size_t)(row_base + rr);
+    src_row = (size_t)(row_base + rr);
     aon[s] = true;
     if constexpr (OP == OP_ROUTER) aon[s] = valid == nullptr || valid[src_row] != 0;
     aoff[s] = (uint32_t)(src_row * K) + kofs + 8 * asq;
@@ -151,7 +150,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   int bslot[BP], bslot2[BP], bsr[BP];
   {
     size_t base = 0;
-    if constexpr (OP == OP_GATE_UP) base = (size_t)e * 2 * I * H;
     if constexpr (OP == OP_DOWN) base = (size_t)e * H * I;
     wexp = FP8 ? static_cast<const void*>(static_cast<const uint8_t*>(w) + base)
                : static_cast<const void*>(static_cast<const uint16_t*>(w) + base);
@@ -163,8 +161,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
         const int l0 = FP8 ? 2 * (P & 31) : (P & 63);
         const int lt = blk >> 1, j = blk & 1;
         int gt;   // 16-row tile of the expert's matrix
-        if constexpr (OP == OP_GATE_UP) gt = (lt < 8 ? 0 : I / 16 - 8) + nt * 8 + lt;
-        else gt = min(nt * 16 + lt, H / 16 - 1);
+        gt = min(nt * 16 + lt, H / 16 - 1);
         boff[s] = ((uint32_t)gt * (K / 32) + kofs / 32 + j) * 512 + 8 * l0;
         bslot[s] = (lt * 2 + j) * kWave + swz(l0, j);
         bslot2[s] = (lt * 2 + j) * kWave + swz(l0 + 1, j);
@@ -172,14 +169,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(
       } else {
         const int wr = FP8 ? (tid >> 2) + 64 * s : (tid >> 3) + 32 * s;
         const int piece = FP8 ? (tid & 3) : (tid & 7);
-        int grow, nrows;
-        if constexpr (OP == OP_GATE_UP) {
-          grow = (wr < 128 ? 0 : I - 128) + nt * 128 + wr;
-          nrows = 2 * I;
-        } else {
-          grow = nt * kBN + wr;
-          nrows = OP == OP_DOWN ? H : E;
-        }
+        int grow = nt * kBN + wr;
+        const int nrows = OP == OP_DOWN ? H : E;
         grow = min(grow, nrows - 1);
         boff[s] = (uint32_t)grow * K + kofs + (FP8 ? 16 : 8) * piece;
         const int j = FP8 ? (piece >> 1) : (piece >> 2);
@@ -191,20 +182,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     }
   }
   // fp8: weight rows wr < 128 of the tile use scale row 0, the others row 1
-  // (gate/up: the gate and the up 128-row block; down: rows nt*256 + 0..255)
+  // (rows nt*256 + 0..255 of W2)
   if constexpr (FP8) {
     const int nkb = K / 128;
-    int sr0, sr1;
-    const float* sb;
-    if constexpr (OP == OP_GATE_UP) {
-      sb = wscale + (size_t)e * (2 * I / 128) * nkb;
-      sr0 = nt;
-      sr1 = I / 128 + nt;
-    } else {
-      sb = wscale + (size_t)e * (H / 128) * nkb;
-      sr0 = min(2 * nt, H / 128 - 1);
-      sr1 = min(2 * nt + 1, H / 128 - 1);
-    }
+    const float* sb = wscale + (size_t)e * (H / 128) * nkb;
+    const int sr0 = min(2 * nt, H / 128 - 1);
+    const int sr1 = min(2 * nt + 1, H / 128 - 1);
     for (int i = tid; i < 2 * nkb; i += 256)
       sscale[i / nkb][i % nkb] = sb[(size_t)(i < nkb ? sr0 : sr1) * nkb + i % nkb];
   }
@@ -251,10 +234,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[mt][q] = floatx4{0.f, 0.f, 0.f, 0.f};
   // LDS weight tile of wave column wn, tile q
-  auto btile = [&](int q) -> int {
-    if constexpr (OP == OP_GATE_UP) return (q < 4 ? 0 : 8) + wn * 4 + (q & 3);
-    else return wn * 8 + q;
-  };
+  auto btile = [&](int q) -> int { return wn * 8 + q; };
   auto compute = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -310,20 +290,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 64 + mt * 16 + 4 * g + i;
       if (row >= rows_here) continue;
-      if constexpr (OP == OP_GATE_UP) {
-        uint16_t* hr = static_cast<uint16_t*>(dst) + (size_t)(row_base + row) * I;
+      const int ncols = OP == OP_DOWN ? H : E;
+      float* yr = static_cast<float*>(dst) + (size_t)z * T * E + (size_t)(row_base + row) * ncols;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          hr[nt * 128 + (wn * 4 + q) * 16 + m] =
-              f32_to_bf16_bits(silu_mul(acc[mt][q][i], acc[mt][q + 4][i]));
-      } else {
-        const int ncols = OP == OP_DOWN ? H : E;
-        float* yr = static_cast<float*>(dst) + (size_t)z * T * E + (size_t)(row_base + row) * ncols;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int n = nt * kBN + (wn * 8 + q) * 16 + m;
-          if (n < ncols) yr[n] = acc[mt][q][i];
-        }
+      for (int q = 0; q < 8; ++q) {
+        const int n = nt * kBN + (wn * 8 + q) * 16 + m;
+        if (n < ncols) yr[n] = acc[mt][q][i];
       }
     }
 }
@@ -437,6 +409,160 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   }
 }
 
+// Gate/up of the large segments: 128 sorted rows x (128 gate + the matching
+// 128 up columns) per block, with the roles of down_tall_kernel: each wave owns 32 gate and the matching 32 up columns,
+// whose W13 fragments it loads straight from memory (the MFMA A operand,
+// fp8 dequantised in registers, two 64-wide K windows ahead), while the x
+// rows of the window come through LDS (shared by the four waves, two
+// buffers, one barrier per window).  A lane ends with 4 consecutive gate
+// columns and the same 4 up columns of one row, so SiLU(g) * u is formed in
+// registers and stored as 8 bytes.
+template <bool FP8, bool PW>
+__global__ __launch_bounds__(256) void gate_up_tall_kernel(
+    const uint16_t* __restrict__ x, const void* __restrict__ w13, const float* __restrict__ s13,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ tile_seg,
+    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ n_tiles_ptr,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    uint16_t* __restrict__ h, int H, int I, int k, int n_nt, int max_tiles) {
+  __shared__ u32x4 xbuf[2][kASlots][kWave];   // 2 x 16 KB
+  __shared__ float sscale[2][kMaxScaleCols];  // fp8: gate / up scale rows
+  const int lid = xcd_remap_g(blockIdx.x, gridDim.x);
+  if (lid >= max_tiles * n_nt) return;
+  const int mt_id = lid / n_nt, nt = lid - mt_id * n_nt;
+  if (mt_id >= *n_tiles_ptr) return;
+  const int e = tile_seg[mt_id];
+  const int r0 = tile_row0[mt_id];
+  const int row_base = seg_off[e] + r0;
+  const int rows_here = min(kBM, seg_cnt[e] - r0);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int m = lane % 16, g = lane / 16;
+
+  // x staging: 4 x 16 B per thread per window, as gemm_kernel's A operand
+  const int asq = tid & 7;
+  uint32_t aoff[4];
+  int aslot[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int row = (tid >> 3) + 32 * s;
+    const int rr = min(row, rows_here - 1);
+    aoff[s] = (uint32_t)((size_t)(sorted_ids[row_base + rr] / k) * H) + 8 * asq;
+    const int j = asq >> 2, l = (asq & 3) * 16 + (row & 15);
+    aslot[s] = ((row >> 4) * 2 + j) * kWave + swz(l, j);
+  }
+  // W13 fragments of this wave: tiles q = 0, 1 gate (16 rows each), q = 2, 3
+  // the matching up rows; element offset of step 0 and of one K step
+  const size_t wexp = (size_t)e * 2 * I * H;
+  size_t woff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (q < 2 ? 0 : I) + nt * 128 + wave * 32 + (q & 1) * 16;
+    if constexpr (PW) woff[q] = wexp + (size_t)(row / 16) * (H / 32) * 512 + 8 * lane;
+    else woff[q] = wexp + (size_t)(row + m) * H + 8 * g;
+  }
+  constexpr size_t wstep = PW ? 512 : 32;
+  if constexpr (FP8) {
+    const int nkb = H / 128;
+    const float* sb = s13 + (size_t)e * (2 * I / 128) * nkb;
+    for (int i = tid; i < 2 * nkb; i += 256)
+      sscale[i / nkb][i % nkb] = sb[(size_t)(i < nkb ? nt : I / 128 + nt) * nkb + i % nkb];
+  }
+
+  struct XStage { u32x4 a[4]; };
+  struct WStage { typename std::conditional<FP8, u32x2, u32x4>::type c[2][4]; };
+  auto x_load = [&](XStage& S, int win) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      S.a[s] = *reinterpret_cast<const u32x4*>(x + aoff[s] + (uint32_t)win * kKW);
+  };
+  auto x_store = [&](const XStage& S, int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) (&xbuf[buf][0][0])[aslot[s]] = S.a[s];
+  };
+  auto w_load = [&](WStage& W, int win) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const size_t o = woff[q] + (size_t)(2 * win + j) * wstep;
+        if constexpr (FP8) W.c[j][q] = ld8(static_cast<const uint8_t*>(w13) + o);
+        else W.c[j][q] = ld16(static_cast<const uint16_t*>(w13) + o);
+      }
+  };
+  floatx4 acc[4][8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const WStage& W, int buf, int win) {
+    float sg = 1.f, su = 1.f;
+    if constexpr (FP8) {
+      sg = sscale[0][win >> 1];
+      su = sscale[1][win >> 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      bf16x8 wa[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (FP8) wa[q] = fp8x8_scaled(W.c[j][q], q < 2 ? sg : su);
+        else wa[q] = as_bf16x8(W.c[j][q]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        const bf16x8 xb = __builtin_bit_cast(bf16x8, xbuf[buf][mt * 2 + j][swz(lane, j)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q][mt] = mfma16x16x32(wa[q], xb, acc[q][mt]);
+      }
+    }
+  };
+
+  // windows in pairs (the count H / 64 is even): stage names fixed, loads two
+  // windows ahead (past the end they re-read the last window, unused)
+  const int nwin = H / kKW, last = nwin - 1;
+  XStage xs0, xs1;
+  WStage ws0, ws1;
+  x_load(xs0, 0);
+  w_load(ws0, 0);
+  x_load(xs1, min(1, last));
+  w_load(ws1, min(1, last));
+  __syncthreads();   // scale rows
+  x_store(xs0, 0);
+  __syncthreads();
+  x_load(xs0, min(2, last));
+  for (int win = 0; win < nwin; win += 2) {
+    compute(ws0, 0, win);
+    w_load(ws0, min(win + 2, last));
+    x_store(xs1, 1);
+    __syncthreads();
+    x_load(xs1, min(win + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ws1, 1, win + 1);
+    w_load(ws1, min(win + 3, last));
+    x_store(xs0, 0);
+    __syncthreads();
+    x_load(xs0, min(win + 4, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // acc[q][mt] lane (m, g) element i: column 32 wave + 16 (q & 1) + 4 g + i of
+  // the block's 128 (gate for q < 2, up for q >= 2), sorted row mt * 16 + m
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int row = mt * 16 + m;
+    if (row >= rows_here) continue;
+    uint16_t* hr = h + (size_t)(row_base + row) * I + nt * 128 + wave * 32;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(silu_mul(acc[q][mt][0], acc[q + 2][mt][0]),
+                          silu_mul(acc[q][mt][1], acc[q + 2][mt][1]));
+      pk[1] = pack_bf16x2(silu_mul(acc[q][mt][2], acc[q + 2][mt][2]),
+                          silu_mul(acc[q][mt][3], acc[q + 2][mt][3]));
+      *reinterpret_cast<u32x2*>(hr + 16 * q + 4 * g) = pk;
+    }
+  }
+}
+
 int round8g(int v) { return (v + 7) / 8 * 8; }
 
 template <int OP, bool FP8, bool PW>
@@ -477,9 +603,16 @@ hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void*
                                int max_tiles, hipStream_t s) {
   if (H % 128 != 0 || I % 128 != 0 || H > kMaxGemmK) return hipErrorInvalidValue;
   const int n_nt = I / 128;
-  launch_gemm_w<OP_GATE_UP>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
-                            static_cast<const uint16_t*>(x), w13, s13, sorted_ids, tile_seg,
-                            tile_row0, n_tiles, seg_off, seg_cnt, h, H, I, k, n_nt, max_tiles);
+  const dim3 grid(round8g(max_tiles * n_nt));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+#define MOE_GUT(F8, P)                                                                      \
+  hipLaunchKernelGGL((gate_up_tall_kernel<F8, P>), grid, dim3(256), 0, s, xb, w13, s13,     \
+                     sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, hb, H, I, k, \
+                     n_nt, max_tiles)
+  if (fp8) { if (packed) MOE_GUT(true, true); else MOE_GUT(true, false); }
+  else { if (packed) MOE_GUT(false, true); else MOE_GUT(false, false); }
+#undef MOE_GUT
   return hipGetLastError();
 }
 

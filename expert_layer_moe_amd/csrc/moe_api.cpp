@@ -70,8 +70,11 @@ int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
   return MOE_OK;
 }
 
+// The tiled kernels index x with 32-bit element offsets.
+bool fits_tiled(const moe_desc* d) { return (long long)d->T * d->H < (1LL << 31); }
+
 bool use_router_gemm(const moe_desc* d) {
-  return d->act_dtype == MOE_BF16 && d->T >= 1024 && d->H % 128 == 0;
+  return d->act_dtype == MOE_BF16 && d->T >= 1024 && d->H % 128 == 0 && fits_tiled(d);
 }
 
 // K split of the router logits (the top-k kernel sums the ks partials in a
@@ -102,7 +105,7 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->router_gemm = use_router_gemm(d);
   const int min_rows = g_gemm_min_rows.load();
   p->big_thr = (d->act_dtype == MOE_BF16 && d->I % 128 == 0 && d->H <= moe::kMaxGemmK &&
-                d->I <= moe::kMaxGemmK)
+                d->I <= moe::kMaxGemmK && fits_tiled(d))
                    ? min_rows
                    : INT_MAX;
   const size_t kk = (size_t)topk + p->ns;
