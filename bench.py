@@ -129,6 +129,8 @@ def run(args):
     from workloads import get_config, make_inputs
 
     moe.load_library()
+    if args.gemm_min_rows is not None:
+        moe.moe_set_path_thresholds(args.gemm_min_rows, args.gemm_min_tiles)
     if args.copy_calibrate:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -267,7 +269,9 @@ def run(args):
                    "H": cfg.H, "E": cfg.E, "topk": cfg.k, "I": cfg.I,
                    "n_shared": cfg.n_shared, "weights": cfg.w,
                    "weight_layout": "frag16" if packed else "row_major",
-                   "two_streams": pair},
+                   "two_streams": pair,
+                   "gemm_thresholds": (None if args.gemm_min_rows is None
+                                       else [args.gemm_min_rows, args.gemm_min_tiles])},
     }
     if not pair:
         g_ms, g_n = dom_rec[dom]
@@ -318,6 +322,10 @@ def main():
     ap.add_argument("--config", default="decode_e48")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibrate", action="store_true")
+    ap.add_argument("--gemm-min-rows", type=int, default=None,
+                    help="segments above this many rows may take the tiled GEMM kernels")
+    ap.add_argument("--gemm-min-tiles", type=int, default=-1,
+                    help="... once their 128-row tiles number this many (-1: fill the chip)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay pass")
     ap.add_argument("--row-major", action="store_true",
