@@ -331,3 +331,33 @@ def test_two_stream_pair_replays_in_a_hip_graph():
         g.replay()
         torch.cuda.synchronize()
         assert all(torch.equal(o, r) for o, r in zip(outs, ref)), f"replay {i}"
+
+
+# ------------------------------------------------------------ random shapes --
+def _random_shape(seed):
+    """A seeded layer shape within what the ABI accepts for bf16 activations."""
+    r = np.random.default_rng(1000 + seed)
+    w = ["bf16", "fp8"][r.integers(2)]
+    H = int(r.choice([128, 256, 384, 512, 768]))
+    I = int(r.choice([128, 256, 384]) if w == "fp8" else r.choice([32, 64, 96, 128, 160, 256]))
+    E = int(r.choice([1, 2, 3, 5, 8, 13, 16, 33, 64, 128]))
+    k = int(r.integers(1, min(8, E) + 1))
+    T = int(r.choice([1, 2, 7, 16, 31, 64, 100, 257, 513, 700]))
+    ns = int(r.integers(2))
+    vf = float(r.choice([1.0, 1.0, 0.75, 0.3]))
+    return dict(T=T, H=H, E=E, k=k, I=I, n_shared=ns, w=w, valid_frac=vf)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_match_oracle(seed):
+    """Seeded random shapes (ragged T, E from 1 to 128, k up to 8, shared
+    expert, fp8, padding rows), packed weights, both expert paths."""
+    kw = _random_shape(seed)
+    log(f"[case] random shape {seed}: {kw}")
+    inp = random_small(seed=500 + seed, **kw)
+    layer = device_layer(inp, packed=True)
+    gpu = run_gpu(inp, layer)
+    compare(inp, gpu)
+    if _gemm_capable(kw):
+        with gemm_path():
+            compare(inp, run_gpu(inp, layer))
