@@ -373,38 +373,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
       for (int kb = 0; kb < KSTEPS / 4; ++kb) sk[kb] = sc[(n0 / 128) * (I / 128) + kb];
     }
-    floatx4 acc[4][8];
+    // two 32-column halves: the y stores of the first overlap the MFMAs of
+    // the second
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int hq = 0; hq < 2; ++hq) {
+      const int nh = n0 + 32 * hq;
+      floatx4 acc[2][8];
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int st = 0; st < KSTEPS; ++st) {
-      bf16x8 wa[4];
+        for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (FP8)
-          wa[q] = fp8x8_scaled(ld8(static_cast<const uint8_t*>(w2) + woff(n0 + 16 * q, st)),
-                               sk[st / 4]);
-        else
-          wa[q] = as_bf16x8(ld16(static_cast<const uint16_t*>(w2) + woff(n0 + 16 * q, st)));
+      for (int st = 0; st < KSTEPS; ++st) {
+        bf16x8 wa[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if constexpr (FP8)
+            wa[q] = fp8x8_scaled(ld8(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st)),
+                                 sk[st / 4]);
+          else
+            wa[q] = as_bf16x8(ld16(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st)));
+        }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
+        const int row = mt * 16 + m;
+        if (row >= rows_here) continue;
+        float* yr = y + (size_t)(row_base + row) * H;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
+        for (int q = 0; q < 2; ++q) *reinterpret_cast<floatx4*>(yr + nh + 16 * q + 4 * g) = acc[q][mt];
       }
-    }
-    // acc[q][mt] lane (m, g) element i: output column n0 + 16 q + 4 g + i of
-    // tile row mt * 16 + m (16-byte stores; H is a multiple of 64)
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const int row = mt * 16 + m;
-      if (row >= rows_here) continue;
-      float* yr = y + (size_t)(row_base + row) * H;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) *reinterpret_cast<floatx4*>(yr + n0 + 16 * q + 4 * g) = acc[q][mt];
     }
   }
 }
