@@ -79,12 +79,11 @@ __device__ __forceinline__ int swz(int l, int j) { return l ^ (((l >> 4) << 1) |
 template <int OP, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void gemm_kernel(
     const uint16_t* __restrict__ a_src, const void* __restrict__ w,
-    const float* __restrict__ wscale, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
-    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, const uint8_t* __restrict__ valid,
-    void* __restrict__ dst, int H, int I, int k, int n_nt, int max_tiles, int T, int E,
-    int ksplit) {
+    const float* __restrict__ wscale, const int32_t* __restrict__ tile_seg,
+    const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ n_tiles_ptr,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    const uint8_t* __restrict__ valid, void* __restrict__ dst, int H, int I, int n_nt,
+    int max_tiles, int T, int E, int ksplit) {
   __shared__ u32x4 abuf[2][kASlots][kWave];   // 2 x 16 KB
   __shared__ u32x4 bbuf[2][kBSlots][kWave];   // 2 x 32 KB
   __shared__ float sscale[2][kMaxScaleCols];  // fp8: the two 128-row scale rows
@@ -571,22 +570,20 @@ int round8g(int v) { return (v + 7) / 8 * 8; }
 
 template <int OP, bool FP8, bool PW>
 void launch_gemm(dim3 grid, hipStream_t s, const uint16_t* a, const void* w, const float* ws,
-                 const int32_t* sorted_ids, const int32_t* tseg, const int32_t* trow,
-                 const int32_t* ntiles, const int32_t* seg_off, const int32_t* seg_cnt,
-                 void* dst, int H, int I, int k, int n_nt, int max_tiles) {
-  hipLaunchKernelGGL((gemm_kernel<OP, FP8, PW>), grid, dim3(256), 0, s, a, w, ws, sorted_ids,
-                     tseg, trow, ntiles, seg_off, seg_cnt, nullptr, dst, H, I, k, n_nt,
-                     max_tiles, 0, 0, 1);
+                 const int32_t* tseg, const int32_t* trow, const int32_t* ntiles,
+                 const int32_t* seg_off, const int32_t* seg_cnt, void* dst, int H, int I,
+                 int n_nt, int max_tiles) {
+  hipLaunchKernelGGL((gemm_kernel<OP, FP8, PW>), grid, dim3(256), 0, s, a, w, ws, tseg, trow,
+                     ntiles, seg_off, seg_cnt, nullptr, dst, H, I, n_nt, max_tiles, 0, 0, 1);
 }
 
 template <int OP>
 void launch_gemm_w(bool fp8, bool packed, dim3 grid, hipStream_t s, const uint16_t* a,
-                   const void* w, const float* ws, const int32_t* sorted_ids,
-                   const int32_t* tseg, const int32_t* trow, const int32_t* ntiles,
-                   const int32_t* seg_off, const int32_t* seg_cnt, void* dst, int H, int I,
-                   int k, int n_nt, int max_tiles) {
-#define MOE_GEMM_ARGS grid, s, a, w, ws, sorted_ids, tseg, trow, ntiles, seg_off, seg_cnt, dst, \
-                      H, I, k, n_nt, max_tiles
+                   const void* w, const float* ws, const int32_t* tseg, const int32_t* trow,
+                   const int32_t* ntiles, const int32_t* seg_off, const int32_t* seg_cnt,
+                   void* dst, int H, int I, int n_nt, int max_tiles) {
+#define MOE_GEMM_ARGS grid, s, a, w, ws, tseg, trow, ntiles, seg_off, seg_cnt, dst, H, I, n_nt, \
+                      max_tiles
   if (fp8) {
     if (packed) launch_gemm<OP, true, true>(MOE_GEMM_ARGS);
     else launch_gemm<OP, true, false>(MOE_GEMM_ARGS);
@@ -645,8 +642,8 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
   }
   const int n_nt = (H + kBN - 1) / kBN;
   launch_gemm_w<OP_DOWN>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
-                         static_cast<const uint16_t*>(h), w2, s2, nullptr, tile_seg, tile_row0,
-                         n_tiles, seg_off, seg_cnt, y, H, I, 1, n_nt, max_tiles);
+                         static_cast<const uint16_t*>(h), w2, s2, tile_seg, tile_row0, n_tiles,
+                         seg_off, seg_cnt, y, H, I, n_nt, max_tiles);
   return hipGetLastError();
 }
 
@@ -658,7 +655,7 @@ hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R
   dim3 grid(round8g(tiles * n_nt * ks));
   hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false, false>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), R, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, nullptr, valid, part, H, 0, 1, n_nt, tiles, T, E, ks);
+                     nullptr, nullptr, valid, part, H, 0, n_nt, tiles, T, E, ks);
   return hipGetLastError();
 }
 
