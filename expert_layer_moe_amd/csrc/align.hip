@@ -40,10 +40,13 @@ __device__ __forceinline__ int seg_of(const int32_t* ids, int a, int k, int kk,
 
 // Exclusive scan of the padded segment counts (cnt in LDS) by wave 0 into
 // base (LDS) and offsets / n_post; wave 1 lists the 128-row tiles of the
-// segments above big_thr rows.  Ends with a barrier.
+// segments above big_thr rows; wave 2 lists the streaming kernels' work
+// items (the rows of every other non-empty segment, kStreamItemRows at a
+// time).  Ends with a barrier.
 __device__ void scan_segments(const int* cnt, int* base, int nseg, int bm, int32_t* offsets,
                               int32_t* n_post, int big_thr, int min_tiles, int32_t* tile_seg,
-                              int32_t* tile_row0, int32_t* n_tiles) {
+                              int32_t* tile_row0, int32_t* n_tiles, int32_t* item_seg,
+                              int32_t* item_row0, int32_t* n_items) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   if (wave == 0) {
     int local[5];
@@ -103,6 +106,43 @@ __device__ void scan_segments(const int* cnt, int* base, int nseg, int bm, int32
       run += local[q];
     }
     if (lane == kWave - 1) *n_tiles = inc >= min_tiles ? inc : 0;
+  } else if (wave == 2 && item_seg != nullptr) {
+    // the GEMM decision of wave 1 (its tile total against min_tiles), then
+    // the items of the segments it leaves to the streaming kernels
+    int c[5];
+    int tiles = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      const int seg = lane * 5 + q;
+      c[q] = seg < nseg ? cnt[seg] : 0;
+      tiles += c[q] > big_thr ? (c[q] + kBigTile - 1) / kBigTile : 0;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) tiles += __shfl_xor(tiles, off);
+    const bool gemm = tile_seg != nullptr && tiles > 0 && tiles >= min_tiles;
+    int local[5];
+    int sum = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      local[q] = (gemm && c[q] > big_thr) ? 0 : (c[q] + kStreamItemRows - 1) / kStreamItemRows;
+      sum += local[q];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(inc, off);
+      if (lane >= off) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) {
+      for (int i = 0; i < local[q]; ++i) {
+        item_seg[run + i] = lane * 5 + q;
+        item_row0[run + i] = i * kStreamItemRows;
+      }
+      run += local[q];
+    }
+    if (lane == kWave - 1) *n_items = inc;
   }
   __syncthreads();
 }
@@ -170,7 +210,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
     int32_t* __restrict__ slot_pos, int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
     int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
-    int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ item_seg,
+    int32_t* __restrict__ item_row0, int32_t* __restrict__ n_items) {
   __shared__ int cnt[kMaxSeg];
   __shared__ int base[kMaxSeg];
   __shared__ int wcnt[kAlignWaves][kMaxSeg];
@@ -190,7 +231,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   }
   __syncthreads();
   scan_segments(cnt, base, nseg, bm, offsets, n_post, big_thr, min_tiles, tile_seg, tile_row0,
-                n_tiles);
+                n_tiles, item_seg, item_row0, n_items);
   pad_segments(cnt, base, nseg, bm, sorted_ids, block_expert, seg_count);
   scatter_range(ids, 0, n_assign, k, kk, E, nseg, base, wcnt, sorted_ids, slot_pos);
 }
@@ -228,7 +269,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ n_post,
     int32_t* __restrict__ seg_count, int big_thr, int min_tiles,
     int32_t* __restrict__ tile_seg, int32_t* __restrict__ tile_row0,
-    int32_t* __restrict__ n_tiles) {
+    int32_t* __restrict__ n_tiles, int32_t* __restrict__ item_seg,
+    int32_t* __restrict__ item_row0, int32_t* __restrict__ n_items) {
   __shared__ int cnt[kMaxSeg];
   __shared__ int base[kMaxSeg];
   const int tid = threadIdx.x;
@@ -240,7 +282,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
   }
   __syncthreads();
   scan_segments(cnt, base, nseg, bm, offsets, n_post, big_thr, min_tiles, tile_seg, tile_row0,
-                n_tiles);
+                n_tiles, item_seg, item_row0, n_items);
   pad_segments(cnt, base, nseg, bm, sorted_ids, block_expert, seg_count);
   for (int seg = tid; seg < nseg; seg += kAlignThreads) {
     int run = base[seg];
@@ -282,19 +324,22 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
                         int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
                         int32_t* tile_row0, int32_t* n_tiles, int32_t* span_buf,
+                        int32_t* item_seg, int32_t* item_row0, int32_t* n_items,
                         hipStream_t s) {
   const int n_span = align_spans(T, k, n_shared);
   if (n_span == 0 || span_buf == nullptr) {
     hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, T, k,
                        E, n_shared, bm, sorted_ids, block_expert, offsets, n_post,
-                       slot_pos, seg_count, big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
+                       slot_pos, seg_count, big_thr, min_tiles, tile_seg, tile_row0, n_tiles,
+                       item_seg, item_row0, n_items);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(align_count_kernel, dim3(n_span), dim3(kAlignThreads), 0, s, ids, T, k, E,
                      n_shared, span_buf);
   hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(kAlignThreads), 0, s, n_span, E, n_shared,
                      bm, span_buf, sorted_ids, block_expert, offsets, n_post, seg_count,
-                     big_thr, min_tiles, tile_seg, tile_row0, n_tiles);
+                     big_thr, min_tiles, tile_seg, tile_row0, n_tiles, item_seg, item_row0,
+                     n_items);
   hipLaunchKernelGGL(align_scatter_kernel, dim3(n_span), dim3(kAlignThreads), 0, s, ids, T, k,
                      E, n_shared, span_buf, sorted_ids, slot_pos);
   return hipGetLastError();

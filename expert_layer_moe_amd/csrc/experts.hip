@@ -14,6 +14,8 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+#include <climits>
+
 namespace moe {
 namespace {
 
@@ -34,15 +36,28 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
 }
 
+// Logical id of this block among n_live live blocks of a grid sized for the
+// worst case, or -1 for a surplus block.  The live ids are remapped over the
+// first round_up(n_live, 8) blocks (dispatched first, spread over all XCDs),
+// not over the whole grid, which would leave the later XCDs idle.
+__device__ __forceinline__ int live_block(int n_live) {
+  const int nb = (n_live + 7) & ~7;
+  if ((int)blockIdx.x >= nb) return -1;
+  const int lid = xcd_remap(blockIdx.x, nb);
+  return lid < n_live ? lid : -1;
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming gate/up for expert segments of a few tiles of rows (the
-// decode regime, bound by HBM): one block per (expert, 4/KS groups of 16
-// intermediate columns).  The block's waves split K = H into KS contiguous
-// parts; a wave streams its part of 16 gate rows and the 16 matching up rows
-// of W13 exactly once per pass over up to MT 16-row tiles of the expert's
-// tokens, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
+// decode regime, bound by HBM): one block per (work item, 4/KS groups of 16
+// intermediate columns), a work item being a segment and up to MT = 4 of its
+// 16-row tiles (the align's stream item table; a segment's items run side by
+// side, so its weights come from HBM once and are shared through L2).  The
+// block's waves split K = H into KS contiguous parts; a wave streams its part
+// of 16 gate rows and the 16 matching up rows of W13 once for the item's
+// tiles, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
 // of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
-// grid.x = round_up(n_seg * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
+// grid.x = round_up(max_items * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
 // bf16: three waves per SIMD (164 VGPRs, no spills) keep more weight loads in
 // flight; the fp8 variant keeps two (it would spill).
 template <int KS, int MT, int KU, bool FP8, bool PW>
@@ -50,15 +65,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 ? 2 : 3
 void gate_up_stream_kernel(
     const uint16_t* __restrict__ xp, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ h, int H, int I, int n_seg,
-    int n_cg, int big_thr, const int32_t* __restrict__ gemm_tiles) {
+    const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
+    const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
+    uint16_t* __restrict__ h, int H, int I, int max_items, int n_cg) {
+  static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
   constexpr int CGW = 4 / KS;
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  if (lid >= n_seg * n_cg) return;
-  const int e = lid / n_cg, cgb = lid - e * n_cg;
+  const int lid = live_block(min(*n_items, max_items) * n_cg);
+  if (lid < 0) return;
+  const int item = lid / n_cg, cgb = lid - item * n_cg;
+  const int e = item_seg[item];
   const int cnt = seg_cnt[e];
-  if (cnt == 0 || (cnt > big_thr && *gemm_tiles > 0)) return;   // the tiled GEMM's rows
   const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int ks = wave % KS, cw = wave / KS;
@@ -88,8 +105,9 @@ void gate_up_stream_kernel(
     su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
   }
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int ntiles = (cnt + 15) >> 4;
-  for (int t0 = 0; t0 < ntiles; t0 += MT) {
+  // the item's 16-row tiles [tb, te) of the segment
+  const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+  for (int t0 = tb; t0 < te; t0 += MT) {
     // fragment-ordered token tiles (row0 is a multiple of 16); step s of
     // tile t at xa + 512 s
     const uint16_t* xa[MT];
@@ -114,7 +132,7 @@ void gate_up_stream_kernel(
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            a[u][mt] = as_bf16x8(t0 + mt < ntiles ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+            a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
         if constexpr (FP8) {
           floatx4 pg[MT], pu[MT];
 #pragma unroll
@@ -126,7 +144,7 @@ void gate_up_stream_kernel(
           for (int u = 0; u < KU; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < ntiles) {
+              if (t0 + mt < te) {
                 pg[mt] = mfma16x16x32(a[u][mt], bg[u], pg[mt]);
                 pu[mt] = mfma16x16x32(a[u][mt], bu[u], pu[mt]);
               }
@@ -144,7 +162,7 @@ void gate_up_stream_kernel(
           for (int u = 0; u < KU; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < ntiles) {
+              if (t0 + mt < te) {
                 ag[mt] = mfma16x16x32(a[u][mt], bg[u], ag[mt]);
                 au[mt] = mfma16x16x32(a[u][mt], bu[u], au[mt]);
               }
@@ -171,7 +189,7 @@ void gate_up_stream_kernel(
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        if ((mt % KS) == ks && t0 + mt < ntiles && col_ok) {
+        if ((mt % KS) == ks && t0 + mt < te && col_ok) {
           floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
 #pragma unroll
           for (int q = 1; q < KS; ++q) {
@@ -195,21 +213,23 @@ void gate_up_stream_kernel(
   }
 }
 
-// Weight-streaming down projection: one block per (expert, 64*NT output
-// columns); each wave streams NT 16-row tiles of W2 (full K = I) once per pass
-// over up to MT 16-row tiles of the expert's h rows.  y rows are fp32.
-// grid.x = round_up(n_seg * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
+// Weight-streaming down projection: one block per (work item, 64*NT output
+// columns); each wave streams NT 16-row tiles of W2 (full K = I) once for
+// the item's (up to MT) 16-row tiles of h.  y rows are fp32.
+// grid.x = round_up(max_items * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
 template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int I,
-    int n_seg, int n_ng, int big_thr, const int32_t* __restrict__ gemm_tiles) {
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  if (lid >= n_seg * n_ng) return;
-  const int e = lid / n_ng, ngb = lid - e * n_ng;
+    const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
+    const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
+    float* __restrict__ y, int H, int I, int max_items, int n_ng) {
+  static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
+  const int lid = live_block(min(*n_items, max_items) * n_ng);
+  if (lid < 0) return;
+  const int item = lid / n_ng, ngb = lid - item * n_ng;
+  const int e = item_seg[item];
   const int cnt = seg_cnt[e];
-  if (cnt == 0 || (cnt > big_thr && *gemm_tiles > 0)) return;   // the tiled GEMM's rows
   const int row0 = seg_off[e];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int n0 = (ngb * 4 + wave) * NT * 16;
@@ -226,8 +246,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   const float* sc = nullptr;
   if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int ntiles = (cnt + 15) >> 4;
-  for (int t0 = 0; t0 < ntiles; t0 += MT) {
+  // the item's 16-row tiles [tb, te) of the segment
+  const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+  for (int t0 = tb; t0 < te; t0 += MT) {
     // fragment-ordered h tiles (rows past cnt may hold anything: MFMA rows
     // are independent, and those output rows are never stored)
     const uint16_t* ha[MT];
@@ -250,7 +271,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
       for (int u = 0; u < KU; ++u)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          a[u][mt] = as_bf16x8(t0 + mt < ntiles ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+          a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
       if constexpr (FP8) {
         floatx4 p[MT][NT];
 #pragma unroll
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            if (t0 + mt < ntiles)
+            if (t0 + mt < te)
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], p[mt][nt]);
         const int kb = kk >> 7;
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            if (t0 + mt < ntiles)
+            if (t0 + mt < te)
 #pragma unroll
               for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], acc[mt][nt]);
       }
@@ -359,16 +380,18 @@ struct GuArgs {
   const float* s13;
   const int32_t* seg_off;
   const int32_t* seg_cnt;
+  const int32_t* item_seg;
+  const int32_t* item_row0;
+  const int32_t* n_items;
   uint16_t* h;
-  int H, I, n_seg, n_cg, big_thr;
-  const int32_t* gemm_tiles;
+  int H, I, max_items, n_cg;
 };
 
 template <int KS, int KU, bool FP8, bool PW>
 void launch_gu(const GuArgs& a) {
   hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s,
-                     a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.h, a.H, a.I, a.n_seg, a.n_cg,
-                     a.big_thr, a.gemm_tiles);
+                     a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0,
+                     a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg);
 }
 
 template <int KS, bool FP8, bool PW>
@@ -393,16 +416,18 @@ struct DnArgs {
   const float* s2;
   const int32_t* seg_off;
   const int32_t* seg_cnt;
+  const int32_t* item_seg;
+  const int32_t* item_row0;
+  const int32_t* n_items;
   float* y;
-  int H, I, n_seg, n_ng, big_thr;
-  const int32_t* gemm_tiles;
+  int H, I, max_items, n_ng;
 };
 
 template <int KU, bool FP8, bool PW>
 void launch_dn(const DnArgs& a) {
   hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
-                     a.s2, a.seg_off, a.seg_cnt, a.y, a.H, a.I, a.n_seg, a.n_ng, a.big_thr,
-                     a.gemm_tiles);
+                     a.s2, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0, a.n_items, a.y, a.H,
+                     a.I, a.max_items, a.n_ng);
 }
 
 template <bool FP8, bool PW>
@@ -419,8 +444,9 @@ int round8(int v) { return (v + 7) / 8 * 8; }
 hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
-                          const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          int big_thr, const int32_t* gemm_tiles, const void* xp, void* h,
+                          const int32_t* seg_off, const int32_t* seg_cnt,
+                          const int32_t* item_seg, const int32_t* item_row0,
+                          const int32_t* n_items, int max_items, const void* xp, void* h,
                           int H, int I, int k, int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(gate_up_f32_kernel, dim3(max_rows), dim3(256), 0, s,
@@ -437,9 +463,10 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   const int ku = pick_ku(H / ks);
   const int cgw = 4 / ks;
   const int n_cg = (I / 16 + cgw - 1) / cgw;
-  if (bm != 16) return hipErrorInvalidValue;
-  GuArgs a{dim3(round8(n_seg * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13, seg_off,
-           seg_cnt, static_cast<uint16_t*>(h), H, I, n_seg, n_cg, big_thr, gemm_tiles};
+  if (bm != 16 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
+  GuArgs a{dim3(round8(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
+           seg_off, seg_cnt, item_seg, item_row0, n_items, static_cast<uint16_t*>(h), H, I,
+           max_items, n_cg};
   if (fp8) {
     if (packed) launch_gu_ks<true, true>(ks, ku, a);
     else launch_gu_ks<true, false>(ks, ku, a);
@@ -452,8 +479,9 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
 
 hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
-                       const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                       int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
+                       const int32_t* seg_off, const int32_t* seg_cnt,
+                       const int32_t* item_seg, const int32_t* item_row0,
+                       const int32_t* n_items, int max_items, float* y, int H, int I,
                        int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
@@ -464,8 +492,9 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
   const bool fp8 = wkind == W_FP8;
   const int ku = pick_ku(I);
   const int n_ng = (H + 255) / 256;
-  DnArgs a{dim3(round8(n_seg * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2, seg_off,
-           seg_cnt, y, H, I, n_seg, n_ng, big_thr, gemm_tiles};
+  if ((long long)max_items * n_ng > INT_MAX - 8) return hipErrorInvalidValue;
+  DnArgs a{dim3(round8(max_items * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2,
+           seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng};
   if (fp8) {
     if (packed) launch_dn_ku<true, true>(ku, a);
     else launch_dn_ku<true, false>(ku, a);

@@ -37,6 +37,17 @@ __device__ __forceinline__ int xcd_remap_g(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
 }
 
+// Logical id among n_live live blocks of a grid sized for the tile table's
+// bound, or -1 for a surplus block: the live ids are remapped over the first
+// round_up(n_live, 8) blocks, which spread over all XCDs (remapping over the
+// whole grid would leave the XCDs of its surplus tail idle).
+__device__ __forceinline__ int live_block_g(int n_live) {
+  const int nb = (n_live + 7) & ~7;
+  if ((int)blockIdx.x >= nb) return -1;
+  const int lid = xcd_remap_g(blockIdx.x, nb);
+  return lid < n_live ? lid : -1;
+}
+
 enum GemmOp { OP_DOWN = 1, OP_ROUTER = 2 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -87,9 +98,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   __shared__ u32x4 abuf[2][kASlots][kWave];   // 2 x 16 KB
   __shared__ u32x4 bbuf[2][kBSlots][kWave];   // 2 x 32 KB
   __shared__ float sscale[2][kMaxScaleCols];  // fp8: the two 128-row scale rows
-  const int lid0 = xcd_remap_g(blockIdx.x, gridDim.x);
   const int per_z = max_tiles * n_nt;
-  if (lid0 >= per_z * ksplit) return;
+  // expert ops: ksplit 1, live blocks from the tile table
+  const int lid0 = OP == OP_ROUTER ? xcd_remap_g(blockIdx.x, gridDim.x)
+                                   : live_block_g(min(*n_tiles_ptr, max_tiles) * n_nt);
+  if (lid0 < 0 || lid0 >= per_z * ksplit) return;
   const int z = lid0 / per_z, lid = lid0 - z * per_z;   // router: K chunk z
   const int mt_id = lid / n_nt, nt = lid - mt_id * n_nt;
   int e = 0, row_base, rows_here;
@@ -331,10 +344,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     int max_tiles) {
   constexpr int I = 32 * KSTEPS;
   __shared__ u32x4 hbuf[8 * KSTEPS][kWave];   // (row tile, step) slots, 1 KB each
-  const int lid = xcd_remap_g(blockIdx.x, gridDim.x);
-  if (lid >= max_tiles * n_chunks) return;
+  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
+  if (lid < 0) return;
   const int mt_id = lid / n_chunks, ch = lid - mt_id * n_chunks;
-  if (mt_id >= *n_tiles_ptr) return;
   const int e = tile_seg[mt_id];
   const int r0 = tile_row0[mt_id];
   const int row_base = seg_off[e] + r0;
@@ -429,10 +441,9 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
     uint16_t* __restrict__ h, int H, int I, int k, int n_nt, int max_tiles) {
   __shared__ u32x4 xbuf[2][kASlots][kWave];   // 2 x 16 KB
   __shared__ float sscale[2][kMaxScaleCols];  // fp8: gate / up scale rows
-  const int lid = xcd_remap_g(blockIdx.x, gridDim.x);
-  if (lid >= max_tiles * n_nt) return;
+  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_nt);
+  if (lid < 0) return;
   const int mt_id = lid / n_nt, nt = lid - mt_id * n_nt;
-  if (mt_id >= *n_tiles_ptr) return;
   const int e = tile_seg[mt_id];
   const int r0 = tile_row0[mt_id];
   const int row_base = seg_off[e] + r0;

@@ -28,8 +28,10 @@ struct Plan {
   int big_thr;    // segments with more rows go to the tiled GEMM kernels
   int max_tiles;  // bound on their 128-row tiles
   int min_tiles;  // fewer tiles than this stay on the streaming kernels
+  int max_items;  // bound on the streaming kernels' work items
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
-      off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_span, off_h, off_y, total;
+      off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_iseg, off_irow, off_nitems,
+      off_span, off_h, off_y, total;
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -124,6 +126,7 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
     const size_t bound = (size_t)p->T * kk / 128 + (size_t)p->T * kk / ((size_t)p->big_thr + 1) + 1;
     if (p->T <= p->big_thr || bound < (size_t)p->min_tiles) p->big_thr = INT_MAX;
   }
+  p->max_items = moe::max_stream_items((long long)p->T * kk, p->E + p->ns);
   p->cap = (int)round_up((size_t)p->T * kk + (size_t)(p->E + p->ns) * (p->bm - 1), p->bm);
   const size_t act_h = (p->act == MOE_F32) ? 4 : 2;
   size_t o = 0;
@@ -140,6 +143,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_tseg = take((size_t)p->max_tiles * 4);
   p->off_trow = take((size_t)p->max_tiles * 4);
   p->off_ntiles = take(4);
+  p->off_iseg = take((size_t)p->max_items * 4);
+  p->off_irow = take((size_t)p->max_items * 4);
+  p->off_nitems = take(4);
   p->off_span = take((size_t)moe::align_spans(p->T, p->k, p->ns) * (p->E + p->ns) * 4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
   // y (fp32 rows) also holds the packed token rows of the streaming gate/up
@@ -275,8 +281,8 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
   if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
   if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
                         block_expert, expert_offsets, n_post_padded, nullptr, nullptr,
-                        INT_MAX, 0, nullptr, nullptr, nullptr, nullptr,
-                        static_cast<hipStream_t>(stream)) != hipSuccess)
+                        INT_MAX, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -304,8 +310,10 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   int32_t* tseg = at<int32_t>(ws, p.off_tseg);
   int32_t* trow = at<int32_t>(ws, p.off_trow);
   int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
+  int32_t* iseg = at<int32_t>(ws, p.off_iseg);
+  int32_t* irow = at<int32_t>(ws, p.off_irow);
+  int32_t* nitems = at<int32_t>(ws, p.off_nitems);
   const bool gemm = p.big_thr != INT_MAX;
-  const int nseg = p.E + p.ns;
   void* h = at<void>(ws, p.off_h);
   float* y = at<float>(ws, p.off_y);
   const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
@@ -325,7 +333,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
     StageTimer tm(S_ALIGN, s);
     if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
                           slot, cnt, p.big_thr, p.min_tiles, gemm ? tseg : nullptr, trow,
-                          ntiles, at<int32_t>(ws, p.off_span),
+                          ntiles, at<int32_t>(ws, p.off_span), iseg, irow, nitems,
                           s) != hipSuccess)
       return MOE_ERR_HIP;
   }
@@ -338,9 +346,8 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   {
     StageTimer tm(S_GATE_UP, s);
     if (moe::launch_gate_up(wkind, packed, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
-                            cnt, nseg, p.big_thr, gemm ? ntiles : nullptr, y, h, p.H, p.I,
-                            p.k, p.bm, p.cap,
-                            s) != hipSuccess)
+                            cnt, iseg, irow, nitems, p.max_items, y, h, p.H, p.I, p.k, p.bm,
+                            p.cap, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   if (gemm) {
@@ -352,8 +359,8 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   }
   {
     StageTimer tm(S_DOWN, s);
-    if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, nseg,
-                         p.big_thr, gemm ? ntiles : nullptr, y, p.H, p.I, p.bm, p.cap,
+    if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
+                         irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap,
                          s) != hipSuccess)
       return MOE_ERR_HIP;
   }

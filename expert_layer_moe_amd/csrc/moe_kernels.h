@@ -27,7 +27,10 @@ hipError_t launch_route_topk(const float* part, int ks, const uint8_t* valid,
 // With tile_seg non-null, also lists the 128-row tiles (segment, first row)
 // of every segment with more than big_thr rows, and their number; fewer
 // than min_tiles tiles (too few blocks to fill the chip) are dropped and
-// n_tiles is 0, leaving every segment to the streaming kernels.
+// n_tiles is 0, leaving every segment to the streaming kernels.  With
+// item_seg non-null, lists the streaming kernels' work items: for every
+// non-empty segment they take, its rows in groups of 64 (segment, first row),
+// and their number.
 // Batches of more than 8192 assignments use align_spans(T, k, n_shared) spans
 // and need span_buf (that many x (E + n_shared) int32); with span_buf null
 // one block does the whole list.
@@ -37,10 +40,19 @@ hipError_t launch_align(const int32_t* ids, int T, int k, int E, int n_shared,
                         int32_t* offsets, int32_t* n_post, int32_t* slot_pos,
                         int32_t* seg_count, int big_thr, int min_tiles, int32_t* tile_seg,
                         int32_t* tile_row0, int32_t* n_tiles, int32_t* span_buf,
+                        int32_t* item_seg, int32_t* item_row0, int32_t* n_items,
                         hipStream_t s);
 
 // ---- expert GEMMs ------------------------------------------------------------
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+// Rows of one work item of the streaming kernels (four 16-row MFMA tiles).
+constexpr int kStreamItemRows = 64;
+// Bound on the work items of a batch of n_rows sorted assignments over nseg
+// segments.
+inline int max_stream_items(long long n_rows, int nseg) {
+  return (int)(n_rows / kStreamItemRows + (n_rows < nseg ? n_rows : nseg));
+}
 
 // Largest K (H for gate/up, I for down) the tiled GEMM kernels take (fp8:
 // their per-block table of 128-wide scale blocks).
@@ -53,18 +65,19 @@ hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t
                          const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
                          const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
                          int max_rows, hipStream_t s);
-// h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for every sorted row r
-// (segments seg_off[e] .. + seg_cnt[e] of the sorted list, e < n_seg).
-// Segments with more than big_thr rows are skipped when *gemm_tiles > 0 (the
-// GEMM kernels' share); gemm_tiles may be null when big_thr is INT_MAX.
+// h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for the sorted rows of
+// the stream item table (item_seg, item_row0: a segment and the first of up
+// to 64 of its rows; *n_items of them, at most max_items; segments at
+// seg_off[e] .. + seg_cnt[e] of the sorted list).
 // bf16: the token rows come from xp (launch_pack_x), and h rows of the
 // streaming kernels' segments are written in fragment order too (16-row
 // tiles; the GEMM kernels' rows stay row-major).  fp32 reads x directly.
 hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
-                          const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                          int big_thr, const int32_t* gemm_tiles, const void* xp, void* h,
+                          const int32_t* seg_off, const int32_t* seg_cnt,
+                          const int32_t* item_seg, const int32_t* item_row0,
+                          const int32_t* n_items, int max_items, const void* xp, void* h,
                           int H, int I, int k, int bm, int max_rows, hipStream_t s);
 // Tiled GEMMs for segments with more than big_thr rows (the align's tile
 // table), and the router GEMM for large batches.  K (H, I) % 128 == 0.
@@ -87,8 +100,9 @@ hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R
 // layout launch_gate_up writes).  packed: weights from launch_pack_weights.
 hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
-                       const int32_t* seg_off, const int32_t* seg_cnt, int n_seg,
-                       int big_thr, const int32_t* gemm_tiles, float* y, int H, int I,
+                       const int32_t* seg_off, const int32_t* seg_cnt,
+                       const int32_t* item_seg, const int32_t* item_row0,
+                       const int32_t* n_items, int max_items, float* y, int H, int I,
                        int bm, int max_rows, hipStream_t s);
 // Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
 // K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
