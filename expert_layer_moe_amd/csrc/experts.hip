@@ -215,7 +215,9 @@ void gate_up_stream_kernel(
 
 // Weight-streaming down projection: one block per (work item, 64*NT output
 // columns); each wave streams NT 16-row tiles of W2 (full K = I) once for
-// the item's (up to MT) 16-row tiles of h.  y rows are fp32.
+// the item's (up to MT) 16-row tiles of h.  W2 is the MFMA's A operand, so
+// a lane ends with 4 consecutive output columns of one row, stored as one
+// 16-byte piece of the row's fp32 y.
 // grid.x = round_up(max_items * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
 template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
@@ -249,8 +251,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   // the item's 16-row tiles [tb, te) of the segment
   const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
   for (int t0 = tb; t0 < te; t0 += MT) {
-    // fragment-ordered h tiles (rows past cnt may hold anything: MFMA rows
-    // are independent, and those output rows are never stored)
+    // fragment-ordered h tiles (rows past cnt may hold anything: each token
+    // row feeds only its own output column of the MFMA, never stored)
     const uint16_t* ha[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
           for (int mt = 0; mt < MT; ++mt)
             if (t0 + mt < te)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], p[mt][nt]);
+              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
         const int kb = kk >> 7;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -301,21 +303,21 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
           for (int mt = 0; mt < MT; ++mt)
             if (t0 + mt < te)
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(a[u][mt], b[u][nt], acc[mt][nt]);
+              for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
       }
     }
+    // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = (t0 + mt) * 16 + m;
+      if (r >= cnt) continue;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const int n = n0 + nt * 16 + m;
         if (n0 + nt * 16 >= H) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = (t0 + mt) * 16 + 4 * g + i;
-          if (r < cnt) y[(size_t)(row0 + r) * H + n] = acc[mt][nt][i];
-        }
+        *reinterpret_cast<floatx4*>(y + (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g) =
+            acc[mt][nt];
       }
+    }
   }
 }
 

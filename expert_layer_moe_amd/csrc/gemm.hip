@@ -50,13 +50,6 @@ __device__ __forceinline__ int live_block_g(int n_live) {
 
 enum GemmOp { OP_DOWN = 1, OP_ROUTER = 2 };
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-}
 
 // 16 fp8 codes -> 16 bf16 (value * s, rounded), as two 16-byte halves
 __device__ __forceinline__ void fp8x16_scaled(u32x4 v, float s, u32x4& lo, u32x4& hi) {

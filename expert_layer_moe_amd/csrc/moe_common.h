@@ -26,6 +26,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (a in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // 8 OCP e4m3fn codes (two dwords) -> 8 bf16, exact (every e4m3 value is a
 // bf16 value).  gfx950's scaled converter applies only the exponent of its
 // scale, so the scale here is 1 and block scales are applied elsewhere.
