@@ -26,12 +26,14 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
     const int32_t* __restrict__ seg_cnt, int big_thr, const int32_t* __restrict__ gemm_tiles,
     uint16_t* __restrict__ xp, int H, int k, int kpc) {
   const int tile = blockIdx.x;
-  if (tile * 16 >= *n_post) return;
-  const int cnt = seg_cnt[block_expert[tile]];
-  if (cnt > big_thr && *gemm_tiles > 0) return;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int m = lane % 16, g = lane / 16;
+  // issued together (the slot is inside the list's capacity; past n_post it
+  // holds a stale value that is never used): a short chain of dependent
+  // loads matters in a kernel this small
   const int sid = sorted_ids[tile * 16 + m];
+  if (tile * 16 >= *n_post) return;
+  if (gemm_tiles != nullptr && seg_cnt[block_expert[tile]] > big_thr && *gemm_tiles > 0) return;
   const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
   uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
   const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
@@ -75,14 +77,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
     int H, int k, int ns, void* __restrict__ out, int out_bf16) {
   const int t = blockIdx.x;
-  const bool valid = ids[(size_t)t * k] >= 0;
   const int kk = k + ns;
+  // the row's id, slot positions and weights are loaded together (a padding
+  // row's positions are stale and never used)
+  const bool valid = ids[(size_t)t * k] >= 0;
   int pos[kMaxSlots];
   float wt[kMaxSlots];
 #pragma unroll
   for (int j = 0; j < kMaxSlots; ++j) {
-    pos[j] = (valid && j < kk) ? slot_pos[(size_t)t * kk + j] : 0;
-    wt[j] = (valid && j < k) ? w[(size_t)t * k + j] : 1.f;
+    pos[j] = j < kk ? slot_pos[(size_t)t * kk + j] : 0;
+    wt[j] = j < k ? w[(size_t)t * k + j] : 1.f;
   }
   // NV groups of 4 columns per thread, each group coalesced across the block;
   // all loads of a thread are issued before the sums
