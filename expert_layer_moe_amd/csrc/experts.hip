@@ -36,15 +36,18 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
 }
 
-// Logical id of this block among n_live live blocks of a grid sized for the
-// worst case, or -1 for a surplus block.  The live ids are remapped over the
-// first round_up(n_live, 8) blocks (dispatched first, spread over all XCDs),
-// not over the whole grid, which would leave the later XCDs idle.
-__device__ __forceinline__ int live_block(int n_live) {
-  const int nb = (n_live + 7) & ~7;
+// The streaming kernels loop over n_live work units (known only on the
+// device) in rounds of gridDim.x (a multiple of 8): this block's unit of the
+// round that starts at u0, or -1.  A partial round is remapped over its
+// first round_up(live, 8) blocks, which spread over all XCDs.  Capping the
+// grid, instead of sizing it for the worst case, keeps surplus blocks from
+// holding the CUs' slots while they find they have nothing to do.
+__device__ __forceinline__ int round_unit(int u0, int n_live) {
+  const int rem = min((int)gridDim.x, n_live - u0);
+  const int nb = (rem + 7) & ~7;
   if ((int)blockIdx.x >= nb) return -1;
-  const int lid = xcd_remap(blockIdx.x, nb);
-  return lid < n_live ? lid : -1;
+  const int l = xcd_remap(blockIdx.x, nb);
+  return l < rem ? u0 + l : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -57,7 +60,7 @@ __device__ __forceinline__ int live_block(int n_live) {
 // of 16 gate rows and the 16 matching up rows of W13 once for the item's
 // tiles, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
 // of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
-// grid.x = round_up(max_items * n_cg, 8), n_cg = ceil(I / (16 * 4 / KS)).
+// Units: (item, column group), n_cg = ceil(I / (16 * 4 / KS)) per item.
 // bf16: three waves per SIMD (164 VGPRs, no spills) keep more weight loads in
 // flight; the fp8 variant keeps two (it would spill).
 template <int KS, int MT, int KU, bool FP8, bool PW>
@@ -71,144 +74,147 @@ void gate_up_stream_kernel(
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
   constexpr int CGW = 4 / KS;
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
-  const int lid = live_block(min(*n_items, max_items) * n_cg);
-  if (lid < 0) return;
-  const int item = lid / n_cg, cgb = lid - item * n_cg;
-  const int e = item_seg[item];
-  const int cnt = seg_cnt[e];
-  const int row0 = seg_off[e];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int ks = wave % KS, cw = wave / KS;
-  const int cg = cgb * CGW + cw;
-  const bool col_ok = cg * 16 < I;
-  const int m = lane % 16, g = lane / 16;
-  const int klen = H / KS, kbeg = ks * klen;
-  const int c0 = col_ok ? cg * 16 : 0;
-  // this lane's element offset in the gate / up rows at step 0 of its K
-  // part, and the distance of one MFMA K step (row-major: 32 elements along
-  // the row; fragment-packed: the next 512-element block of the same tile)
-  constexpr size_t wstep = PW ? 512 : 32;
-  size_t wg_off, wu_off;
-  if constexpr (PW) {
-    const size_t tg = ((size_t)e * 2 * I + c0) / 16, tu = tg + I / 16;
-    wg_off = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-    wu_off = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-  } else {
-    wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
-    wu_off = wg_off + (size_t)I * H;
-  }
-  const float* sg = nullptr;
-  const float* su = nullptr;
-  if constexpr (FP8) {
-    const int nkb = H / 128;
-    sg = s13 + ((size_t)e * (2 * I / 128) + c0 / 128) * nkb;
-    su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
-  }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  // the item's 16-row tiles [tb, te) of the segment
-  const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
-  for (int t0 = tb; t0 < te; t0 += MT) {
-    // fragment-ordered token tiles (row0 is a multiple of 16); step s of
-    // tile t at xa + 512 s
-    const uint16_t* xa[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
-    floatx4 ag[MT], au[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      ag[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      au[mt] = ag[mt];
-    }
-    if (col_ok) {
-      for (int kk = 0; kk < klen; kk += 32 * KU) {
-        bf16x8 bg[KU], bu[KU], a[KU][MT];
-#pragma unroll
-        for (int u = 0; u < KU; ++u) {
-          bg[u] = load_w8<FP8>(w13, wg_off + (size_t)(kk / 32 + u) * wstep);
-          bu[u] = load_w8<FP8>(w13, wu_off + (size_t)(kk / 32 + u) * wstep);
-        }
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
-        if constexpr (FP8) {
-          floatx4 pg[MT], pu[MT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-            pu[mt] = pg[mt];
-          }
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < te) {
-                pg[mt] = mfma16x16x32(a[u][mt], bg[u], pg[mt]);
-                pu[mt] = mfma16x16x32(a[u][mt], bu[u], pu[mt]);
-              }
-          const int kb = (kbeg + kk) >> 7;
-          const float scg = sg[kb], scu = su[kb];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              ag[mt][i] = fmaf(scg, pg[mt][i], ag[mt][i]);
-              au[mt][i] = fmaf(scu, pu[mt][i], au[mt][i]);
-            }
-        } else {
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < te) {
-                ag[mt] = mfma16x16x32(a[u][mt], bg[u], ag[mt]);
-                au[mt] = mfma16x16x32(a[u][mt], bu[u], au[mt]);
-              }
-        }
-      }
-    }
-    if constexpr (KS == 1) {
-      if (col_ok) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = (t0 + mt) * 16 + 4 * g + i;
-            if (r < cnt)
-              h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
-          }
-      }
+  const int n_live = min(*n_items, max_items) * n_cg;
+  for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
+    const int lid = round_unit(u0, n_live);
+    if (lid < 0) continue;
+    const int item = lid / n_cg, cgb = lid - item * n_cg;
+    const int e = item_seg[item];
+    const int cnt = seg_cnt[e];
+    const int row0 = seg_off[e];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int ks = wave % KS, cw = wave / KS;
+    const int cg = cgb * CGW + cw;
+    const bool col_ok = cg * 16 < I;
+    const int m = lane % 16, g = lane / 16;
+    const int klen = H / KS, kbeg = ks * klen;
+    const int c0 = col_ok ? cg * 16 : 0;
+    // this lane's element offset in the gate / up rows at step 0 of its K
+    // part, and the distance of one MFMA K step (row-major: 32 elements along
+    // the row; fragment-packed: the next 512-element block of the same tile)
+    constexpr size_t wstep = PW ? 512 : 32;
+    size_t wg_off, wu_off;
+    if constexpr (PW) {
+      const size_t tg = ((size_t)e * 2 * I + c0) / 16, tu = tg + I / 16;
+      wg_off = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+      wu_off = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
     } else {
+      wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
+      wu_off = wg_off + (size_t)I * H;
+    }
+    const float* sg = nullptr;
+    const float* su = nullptr;
+    if constexpr (FP8) {
+      const int nkb = H / 128;
+      sg = s13 + ((size_t)e * (2 * I / 128) + c0 / 128) * nkb;
+      su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
+    }
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // the item's 16-row tiles [tb, te) of the segment
+    const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+    for (int t0 = tb; t0 < te; t0 += MT) {
+      // fragment-ordered token tiles (row0 is a multiple of 16); step s of
+      // tile t at xa + 512 s
+      const uint16_t* xa[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
+      floatx4 ag[MT], au[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        red[wave][0][mt][lane] = ag[mt];
-        red[wave][1][mt][lane] = au[mt];
+        ag[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        au[mt] = ag[mt];
       }
-      __syncthreads();
+      if (col_ok) {
+        for (int kk = 0; kk < klen; kk += 32 * KU) {
+          bf16x8 bg[KU], bu[KU], a[KU][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if ((mt % KS) == ks && t0 + mt < te && col_ok) {
-          floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
-#pragma unroll
-          for (int q = 1; q < KS; ++q) {
-            const floatx4 g2 = red[cw * KS + q][0][mt][lane];
-            const floatx4 u2 = red[cw * KS + q][1][mt][lane];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              G[i] += g2[i];
-              U[i] += u2[i];
-            }
+          for (int u = 0; u < KU; ++u) {
+            bg[u] = load_w8<FP8>(w13, wg_off + (size_t)(kk / 32 + u) * wstep);
+            bu[u] = load_w8<FP8>(w13, wu_off + (size_t)(kk / 32 + u) * wstep);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = (t0 + mt) * 16 + 4 * g + i;
-            if (r < cnt) h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+          if constexpr (FP8) {
+            floatx4 pg[MT], pu[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+              pu[mt] = pg[mt];
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te) {
+                  pg[mt] = mfma16x16x32(a[u][mt], bg[u], pg[mt]);
+                  pu[mt] = mfma16x16x32(a[u][mt], bu[u], pu[mt]);
+                }
+            const int kb = (kbeg + kk) >> 7;
+            const float scg = sg[kb], scu = su[kb];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ag[mt][i] = fmaf(scg, pg[mt][i], ag[mt][i]);
+                au[mt][i] = fmaf(scu, pu[mt][i], au[mt][i]);
+              }
+          } else {
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te) {
+                  ag[mt] = mfma16x16x32(a[u][mt], bg[u], ag[mt]);
+                  au[mt] = mfma16x16x32(a[u][mt], bu[u], au[mt]);
+                }
           }
         }
       }
-      __syncthreads();
+      if constexpr (KS == 1) {
+        if (col_ok) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = (t0 + mt) * 16 + 4 * g + i;
+              if (r < cnt)
+                h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
+            }
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          red[wave][0][mt][lane] = ag[mt];
+          red[wave][1][mt][lane] = au[mt];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if ((mt % KS) == ks && t0 + mt < te && col_ok) {
+            floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+              const floatx4 g2 = red[cw * KS + q][0][mt][lane];
+              const floatx4 u2 = red[cw * KS + q][1][mt][lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                G[i] += g2[i];
+                U[i] += u2[i];
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = (t0 + mt) * 16 + 4 * g + i;
+              if (r < cnt) h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 }
@@ -218,7 +224,7 @@ void gate_up_stream_kernel(
 // the item's (up to MT) 16-row tiles of h.  W2 is the MFMA's A operand, so
 // a lane ends with 4 consecutive output columns of one row, stored as one
 // 16-byte piece of the row's fp32 y.
-// grid.x = round_up(max_items * n_ng, 8), n_ng = ceil(H / (64 * NT)) (NT = 4).
+// Units: (item, column group), n_ng = ceil(H / (64 * NT)) per item (NT = 4).
 template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
@@ -227,95 +233,98 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
     float* __restrict__ y, int H, int I, int max_items, int n_ng) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
-  const int lid = live_block(min(*n_items, max_items) * n_ng);
-  if (lid < 0) return;
-  const int item = lid / n_ng, ngb = lid - item * n_ng;
-  const int e = item_seg[item];
-  const int cnt = seg_cnt[e];
-  const int row0 = seg_off[e];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int n0 = (ngb * 4 + wave) * NT * 16;
-  if (n0 >= H) return;
-  const int m = lane % 16, g = lane / 16;
-  constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
-  size_t wo[NT];
+  const int n_live = min(*n_items, max_items) * n_ng;
+  for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
+    const int lid = round_unit(u0, n_live);
+    if (lid < 0) continue;
+    const int item = lid / n_ng, ngb = lid - item * n_ng;
+    const int e = item_seg[item];
+    const int cnt = seg_cnt[e];
+    const int row0 = seg_off[e];
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int n0 = (ngb * 4 + wave) * NT * 16;
+    if (n0 >= H) continue;   // no barriers here: waves go their own way
+    const int m = lane % 16, g = lane / 16;
+    constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
+    size_t wo[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = min(n0 + nt * 16, H - 16);
-    if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
-    else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
-  }
-  const float* sc = nullptr;
-  if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  // the item's 16-row tiles [tb, te) of the segment
-  const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
-  for (int t0 = tb; t0 < te; t0 += MT) {
-    // fragment-ordered h tiles (rows past cnt may hold anything: each token
-    // row feeds only its own output column of the MFMA, never stored)
-    const uint16_t* ha[MT];
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = min(n0 + nt * 16, H - 16);
+      if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
+      else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
+    }
+    const float* sc = nullptr;
+    if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // the item's 16-row tiles [tb, te) of the segment
+    const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+    for (int t0 = tb; t0 < te; t0 += MT) {
+      // fragment-ordered h tiles (rows past cnt may hold anything: each token
+      // row feeds only its own output column of the MFMA, never stored)
+      const uint16_t* ha[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
-    floatx4 acc[MT][NT];
+      for (int mt = 0; mt < MT; ++mt)
+        ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
+      floatx4 acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < I; kk += 32 * KU) {
-      bf16x8 b[KU][NT], a[KU][MT];
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < I; kk += 32 * KU) {
+        bf16x8 b[KU][NT], a[KU][MT];
 #pragma unroll
-      for (int u = 0; u < KU; ++u)
+        for (int u = 0; u < KU; ++u)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          b[u][nt] = load_w8<FP8>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
-#pragma unroll
-      for (int u = 0; u < KU; ++u)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
-      if constexpr (FP8) {
-        floatx4 p[MT][NT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int nt = 0; nt < NT; ++nt)
+            b[u][nt] = load_w8<FP8>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
 #pragma unroll
         for (int u = 0; u < KU; ++u)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
-            if (t0 + mt < te)
+            a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+        if constexpr (FP8) {
+          floatx4 p[MT][NT];
 #pragma unroll
-              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
-        const int kb = kk >> 7;
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (t0 + mt < te)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
+          const int kb = kk >> 7;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (t0 + mt < te)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
+        }
+      }
+      // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = (t0 + mt) * 16 + m;
+        if (r >= cnt) continue;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+          if (n0 + nt * 16 >= H) continue;
+          *reinterpret_cast<floatx4*>(y + (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g) =
+              acc[mt][nt];
         }
-      } else {
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            if (t0 + mt < te)
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
-      }
-    }
-    // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int r = (t0 + mt) * 16 + m;
-      if (r >= cnt) continue;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (n0 + nt * 16 >= H) continue;
-        *reinterpret_cast<floatx4*>(y + (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g) =
-            acc[mt][nt];
       }
     }
   }
@@ -441,6 +450,11 @@ void launch_dn_ku(int ku, const DnArgs& a) {
 
 int round8(int v) { return (v + 7) / 8 * 8; }
 
+// Grid of the streaming kernels: one block per unit up to this many, then
+// blocks loop over units.
+constexpr int kStreamGridCap = 4096;
+int stream_grid(int bound) { return min(round8(bound), kStreamGridCap); }
+
 }  // namespace
 
 hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
@@ -466,7 +480,7 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   const int cgw = 4 / ks;
   const int n_cg = (I / 16 + cgw - 1) / cgw;
   if (bm != 16 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
-  GuArgs a{dim3(round8(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
+  GuArgs a{dim3(stream_grid(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
            seg_off, seg_cnt, item_seg, item_row0, n_items, static_cast<uint16_t*>(h), H, I,
            max_items, n_cg};
   if (fp8) {
@@ -495,7 +509,7 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
   const int ku = pick_ku(I);
   const int n_ng = (H + 255) / 256;
   if ((long long)max_items * n_ng > INT_MAX - 8) return hipErrorInvalidValue;
-  DnArgs a{dim3(round8(max_items * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2,
+  DnArgs a{dim3(stream_grid(max_items * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2,
            seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng};
   if (fp8) {
     if (packed) launch_dn_ku<true, true>(ku, a);
