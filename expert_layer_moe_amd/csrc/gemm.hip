@@ -6,9 +6,9 @@
 // ("AMD Instinct MI355X: ATOM ...": block-scale GEMM; Step3 page: FP8
 // blockscale) are dequantised as value(q) * s in fp32 rounded to bf16.
 //
-//   gate_up_tall_kernel: 128 rows x (128 gate + 128 up columns); weights as
-//     the MFMA A operand straight from memory, x rows through LDS, epilogue
-//     h = SiLU(g) * u.
+//   gate_up_tall_kernel: 128 rows x (128 gate + 128 up columns), 32x32x16
+//     MFMA; weights as the A operand straight from memory, x rows through
+//     LDS, epilogue h = SiLU(g) * u.
 //   down_tall_kernel (K = I <= 256): the 128 h rows resident in LDS, a sweep
 //     over output columns, weights as the A operand; y rows fp32.
 //   gemm_kernel (down for larger I, and the router): 128 rows x 256 weight
@@ -418,13 +418,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // Gate/up of the large segments: 128 sorted rows x (128 gate + the matching
-// 128 up columns) per block, with the roles of down_tall_kernel: each wave owns 32 gate and the matching 32 up columns,
-// whose W13 fragments it loads straight from memory (the MFMA A operand,
-// fp8 dequantised in registers, two 64-wide K windows ahead), while the x
-// rows of the window come through LDS (shared by the four waves, two
-// buffers, one barrier per window).  A lane ends with 4 consecutive gate
-// columns and the same 4 up columns of one row, so SiLU(g) * u is formed in
-// registers and stored as 8 bytes.
+// 128 up columns) per block.  Each wave owns 32 gate and the matching 32 up
+// columns, whose W13 fragments it loads straight from memory (the MFMA A
+// operands, fp8 dequantised in registers, two 64-wide K windows ahead), while
+// the x rows of the window come through LDS (shared by the four waves, two
+// buffers, one barrier per window) as four 32-row B operands of the 32x32x16
+// MFMA.  The weights keep the 16-row fragment order (a lane reads 16 bytes of
+// one of the two 16-row tiles of its 32 rows) and the x window the LDS layout
+// of the 16x16x32 kernels: logical K 8 h + i (h = lane / 32) of MFMA step
+// (j, sub) is the physical K 32 j + 8 (2 sub + h) + i of the window for both
+// operands.  A lane ends with four runs of 4 consecutive gate columns and the
+// same up columns of one row, so SiLU(g) * u is formed in registers and
+// stored as 8 bytes.
 template <bool FP8, bool PW>
 __global__ __launch_bounds__(256) void gate_up_tall_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ w13, const float* __restrict__ s13,
@@ -442,7 +447,7 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
   const int row_base = seg_off[e] + r0;
   const int rows_here = min(kBM, seg_cnt[e] - r0);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int m = lane % 16, g = lane / 16;
+  const int l32 = lane % 32, hh = lane / 32, m = lane % 16;
 
   // x staging: 4 x 16 B per thread per window, as gemm_kernel's A operand
   const int asq = tid & 7;
@@ -456,17 +461,19 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
     const int j = asq >> 2, l = (asq & 3) * 16 + (row & 15);
     aslot[s] = ((row >> 4) * 2 + j) * kWave + swz(l, j);
   }
-  // W13 fragments of this wave: tiles q = 0, 1 gate (16 rows each), q = 2, 3
-  // the matching up rows; element offset of step 0 and of one K step
+  // W13 of this wave: q = 0 its 32 gate rows, q = 1 the matching up rows; this
+  // lane's row l32, K half hh.  Offsets of MFMA step (j, sub) of window win:
+  // woff[q] + (2 win + j) wstep + sub wsub.
   const size_t wexp = (size_t)e * 2 * I * H;
-  size_t woff[4];
+  size_t woff[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = (q < 2 ? 0 : I) + nt * 128 + wave * 32 + (q & 1) * 16;
-    if constexpr (PW) woff[q] = wexp + (size_t)(row / 16) * (H / 32) * 512 + 8 * lane;
-    else woff[q] = wexp + (size_t)(row + m) * H + 8 * g;
+  for (int q = 0; q < 2; ++q) {
+    const int row = q * I + nt * 128 + wave * 32 + l32;
+    if constexpr (PW) woff[q] = wexp + ((size_t)(row / 16) * (H / 32)) * 512 + 8 * (16 * hh + m);
+    else woff[q] = wexp + (size_t)row * H + 8 * hh;
   }
   constexpr size_t wstep = PW ? 512 : 32;
+  constexpr size_t wsub = PW ? 256 : 16;
   if constexpr (FP8) {
     const int nkb = H / 128;
     const float* sb = s13 + (size_t)e * (2 * I / 128) * nkb;
@@ -475,7 +482,7 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
   }
 
   struct XStage { u32x4 a[4]; };
-  struct WStage { typename std::conditional<FP8, u32x2, u32x4>::type c[2][4]; };
+  struct WStage { typename std::conditional<FP8, u32x2, u32x4>::type c[2][2][2]; };  // [j][sub][q]
   auto x_load = [&](XStage& S, int win) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -489,17 +496,21 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const size_t o = woff[q] + (size_t)(2 * win + j) * wstep;
-        if constexpr (FP8) W.c[j][q] = ld8(static_cast<const uint8_t*>(w13) + o);
-        else W.c[j][q] = ld16(static_cast<const uint16_t*>(w13) + o);
-      }
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const size_t o = woff[q] + (size_t)(2 * win + j) * wstep + sub * wsub;
+          if constexpr (FP8) W.c[j][sub][q] = ld8(static_cast<const uint8_t*>(w13) + o);
+          else W.c[j][sub][q] = ld16(static_cast<const uint16_t*>(w13) + o);
+        }
   };
-  floatx4 acc[4][8];
+  floatx16 acc[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][n][r] = 0.f;
   auto compute = [&](const WStage& W, int buf, int win) {
     float sg = 1.f, su = 1.f;
     if constexpr (FP8) {
@@ -507,20 +518,25 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
       su = sscale[1][win >> 1];
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8 wa[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (FP8) wa[q] = fp8x8_scaled(W.c[j][q], q < 2 ? sg : su);
-        else wa[q] = as_bf16x8(W.c[j][q]);
+      for (int sub = 0; sub < 2; ++sub) {
+        bf16x8 wa[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if constexpr (FP8) wa[q] = fp8x8_scaled(W.c[j][sub][q], q == 0 ? sg : su);
+          else wa[q] = as_bf16x8(W.c[j][sub][q]);
+        }
+        // token row 32 n + l32 (16-row tile 2 n + l32 / 16), K group 2 sub + hh
+        const int xl = swz(16 * (2 * sub + hh) + m, j);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const bf16x8 xb =
+              __builtin_bit_cast(bf16x8, xbuf[buf][(2 * n + l32 / 16) * 2 + j][xl]);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) acc[q][n] = mfma32x32x16(wa[q], xb, acc[q][n]);
+        }
       }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 xb = __builtin_bit_cast(bf16x8, xbuf[buf][mt * 2 + j][swz(lane, j)]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q][mt] = mfma16x16x32(wa[q], xb, acc[q][mt]);
-      }
-    }
   };
 
   // windows in pairs (the count H / 64 is even): stage names fixed, loads two
@@ -551,21 +567,21 @@ __global__ __launch_bounds__(256) void gate_up_tall_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // acc[q][mt] lane (m, g) element i: column 32 wave + 16 (q & 1) + 4 g + i of
-  // the block's 128 (gate for q < 2, up for q >= 2), sorted row mt * 16 + m
+  // acc[q][n] lane (l32, hh) register r: column 32 wave + 8 (r / 4) + 4 hh +
+  // r % 4 of the block's 128 (gate q = 0, up q = 1), sorted row 32 n + l32
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int row = mt * 16 + m;
+  for (int n = 0; n < 4; ++n) {
+    const int row = 32 * n + l32;
     if (row >= rows_here) continue;
-    uint16_t* hr = h + (size_t)(row_base + row) * I + nt * 128 + wave * 32;
+    uint16_t* hr = h + (size_t)(row_base + row) * I + nt * 128 + wave * 32 + 4 * hh;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int c = 0; c < 4; ++c) {
       u32x2 pk;
-      pk[0] = pack_bf16x2(silu_mul(acc[q][mt][0], acc[q + 2][mt][0]),
-                          silu_mul(acc[q][mt][1], acc[q + 2][mt][1]));
-      pk[1] = pack_bf16x2(silu_mul(acc[q][mt][2], acc[q + 2][mt][2]),
-                          silu_mul(acc[q][mt][3], acc[q + 2][mt][3]));
-      *reinterpret_cast<u32x2*>(hr + 16 * q + 4 * g) = pk;
+      pk[0] = pack_bf16x2(silu_mul(acc[0][n][4 * c], acc[1][n][4 * c]),
+                          silu_mul(acc[0][n][4 * c + 1], acc[1][n][4 * c + 1]));
+      pk[1] = pack_bf16x2(silu_mul(acc[0][n][4 * c + 2], acc[1][n][4 * c + 2]),
+                          silu_mul(acc[0][n][4 * c + 3], acc[1][n][4 * c + 3]));
+      *reinterpret_cast<u32x2*>(hr + 8 * c) = pk;
     }
   }
 }

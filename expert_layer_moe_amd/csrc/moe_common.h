@@ -57,6 +57,15 @@ __device__ __forceinline__ floatx4 mfma16x16x32(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+
+// D(32x32, fp32) += A(32x16) * B(16x32), bf16 inputs.  Lane l holds
+//   A[l%32][8*(l/32) + i], B[8*(l/32) + i][l%32]  (i < 8)
+//   D[8*(r/4) + 4*(l/32) + r%4][l%32]               (r < 16)
+__device__ __forceinline__ floatx16 mfma32x32x16(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
   return __builtin_bit_cast(bf16x8, v);
 }
