@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // same up columns of one row, so SiLU(g) * u is formed in registers and
 // stored as 8 bytes.
 template <bool FP8, bool PW>
-__global__ __launch_bounds__(256) void gate_up_tall_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_tall_kernel(
     const uint16_t* __restrict__ x, const void* __restrict__ w13, const float* __restrict__ s13,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ tile_seg,
     const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ n_tiles_ptr,
