@@ -19,13 +19,18 @@
 namespace moe {
 namespace {
 
+// One lane's 8 weights of a fragment.  Each weight is read once per call, so
+// the loads are non-temporal: they need not displace the token and h tiles
+// that the blocks of a segment share through the caches.
 template <bool FP8>
 __device__ __forceinline__ bf16x8 load_w8(const void* base, size_t elem_off) {
   if constexpr (FP8) {
-    const u32x2 v = ld8(static_cast<const uint8_t*>(base) + elem_off);
+    const u32x2 v = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + elem_off));
     return fp8x8_to_bf16x8(v[0], v[1]);
   } else {
-    return as_bf16x8(ld16(static_cast<const uint16_t*>(base) + elem_off));
+    return as_bf16x8(__builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem_off)));
   }
 }
 

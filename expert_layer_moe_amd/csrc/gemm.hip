@@ -392,11 +392,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         bf16x8 wa[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
+          // non-temporal: the tile's W2 columns are not read again by this block
           if constexpr (FP8)
-            wa[q] = fp8x8_scaled(ld8(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st)),
+            wa[q] = fp8x8_scaled(__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+                                     static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st))),
                                  sk[st / 4]);
           else
-            wa[q] = as_bf16x8(ld16(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st)));
+            wa[q] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st))));
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {

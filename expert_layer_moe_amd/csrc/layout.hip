@@ -104,7 +104,9 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           if (n[v] < H) {
-            const floatx4 val = *reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]);
+            // y is read once: non-temporal
+            const floatx4 val =
+                __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
           }
