@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
-    float* __restrict__ y, int H, int I, int max_items, int n_ng) {
+    void* __restrict__ y, int H, int I, int max_items, int n_ng) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
   const int n_live = min(*n_items, max_items) * n_ng;
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
@@ -327,8 +327,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           if (n0 + nt * 16 >= H) continue;
-          *reinterpret_cast<floatx4*>(y + (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g) =
-              acc[mt][nt];
+          store_y4<FP8>(y, (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g, acc[mt][nt]);
         }
       }
     }
@@ -435,7 +434,7 @@ struct DnArgs {
   const int32_t* item_seg;
   const int32_t* item_row0;
   const int32_t* n_items;
-  float* y;
+  void* y;
   int H, I, max_items, n_ng;
 };
 
@@ -502,12 +501,12 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
-                       const int32_t* n_items, int max_items, float* y, int H, int I,
+                       const int32_t* n_items, int max_items, void* y, int H, int I,
                        int bm, int max_rows, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
-                       block_expert, n_post, y, H, I, bm);
+                       block_expert, n_post, static_cast<float*>(y), H, I, bm);
     return hipGetLastError();
   }
   const bool fp8 = wkind == W_FP8;

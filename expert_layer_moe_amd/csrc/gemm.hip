@@ -296,11 +296,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(
       const int row = wm * 64 + mt * 16 + 4 * g + i;
       if (row >= rows_here) continue;
       const int ncols = OP == OP_DOWN ? H : E;
-      float* yr = static_cast<float*>(dst) + (size_t)z * T * E + (size_t)(row_base + row) * ncols;
+      // router: fp32 partial logits of K chunk z; down: y rows (bf16 with fp8
+      // weights)
+      const size_t ro = (size_t)(row_base + row) * ncols;
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int n = nt * kBN + (wn * 8 + q) * 16 + m;
-        if (n < ncols) yr[n] = acc[mt][q][i];
+        if (n >= ncols) continue;
+        if constexpr (OP == OP_DOWN && FP8)
+          static_cast<uint16_t*>(dst)[ro + n] = f32_to_bf16_bits(acc[mt][q][i]);
+        else
+          static_cast<float*>(dst)[(size_t)z * T * E + ro + n] = acc[mt][q][i];
       }
     }
 }
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const uint16_t* __restrict__ h, const void* __restrict__ w2, const float* __restrict__ s2,
     const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int n_chunks,
+    const int32_t* __restrict__ seg_cnt, void* __restrict__ y, int H, int n_chunks,
     int max_tiles) {
   constexpr int I = 32 * KSTEPS;
   __shared__ u32x4 hbuf[8 * KSTEPS][kWave];   // (row tile, step) slots, 1 KB each
@@ -412,9 +418,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       for (int mt = 0; mt < 8; ++mt) {
         const int row = mt * 16 + m;
         if (row >= rows_here) continue;
-        float* yr = y + (size_t)(row_base + row) * H;
+        const size_t yr = (size_t)(row_base + row) * H + nh + 4 * g;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) *reinterpret_cast<floatx4*>(yr + nh + 16 * q + 4 * g) = acc[q][mt];
+        for (int q = 0; q < 2; ++q) store_y4<FP8>(y, yr + 16 * q, acc[q][mt]);
       }
     }
   }
@@ -643,7 +649,7 @@ hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void*
 hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2,
                             const float* s2, const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
-                            const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
+                            const int32_t* seg_cnt, void* y, int H, int I, int max_tiles,
                             hipStream_t s) {
   if (I % 128 != 0 || I > kMaxGemmK) return hipErrorInvalidValue;
   if (I == 128 || I == 256) {

@@ -68,12 +68,26 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restric
 }
 
 // Combine: one block per token row; fp32 sum over the k routed slots in slot
-// order, then the shared expert, rounded once.  Padding rows -> 0.
+// order, then the shared expert, rounded once.  Padding rows -> 0.  y rows
+// are fp32, or bf16 (YB) in fp8-weight layers.
 constexpr int kMaxSlots = 17;
 
-template <int NV>
+// 4 consecutive values of a y row as fp32; y is read once: non-temporal
+template <bool YB>
+__device__ __forceinline__ floatx4 load_y4(const void* y, size_t idx) {
+  if constexpr (YB) {
+    const u32x2 v =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(y) + idx));
+    return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                   __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(static_cast<const float*>(y) + idx));
+  }
+}
+
+template <int NV, bool YB>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ y, const int32_t* __restrict__ ids,
+    const void* __restrict__ y, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
     int H, int k, int ns, void* __restrict__ out, int out_bf16) {
   const int t = blockIdx.x;
@@ -104,9 +118,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           if (n[v] < H) {
-            // y is read once: non-temporal
-            const floatx4 val =
-                __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]));
+            const floatx4 val = load_y4<YB>(y, (size_t)pos[j] * H + n[v]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
           }
@@ -158,17 +170,21 @@ hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t row
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
+hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s) {
+  if (H % 4 != 0) return hipErrorInvalidValue;
   // two 4-column groups per thread once there are rows enough to fill the chip
-  if (T >= 256)
-    hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, y, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
-  else
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, y, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  const bool two = T >= 256;
+  const dim3 grid(T, two ? (H + 2047) / 2048 : (H + 1023) / 1024);
+  const int ob = out_bf16 ? 1 : 0;
+#define MOE_COMBINE(NV, YB)                                                                 \
+  hipLaunchKernelGGL((combine_kernel<NV, YB>), grid, dim3(256), 0, s, y, ids, w, slot_pos, T, \
+                     H, k, n_shared, out, ob)
+  if (y_bf16) { if (two) MOE_COMBINE(2, true); else MOE_COMBINE(1, true); }
+  else { if (two) MOE_COMBINE(2, false); else MOE_COMBINE(1, false); }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

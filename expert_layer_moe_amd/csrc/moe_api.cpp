@@ -148,9 +148,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_nitems = take(4);
   p->off_span = take((size_t)moe::align_spans(p->T, p->k, p->ns) * (p->E + p->ns) * 4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
-  // y (fp32 rows) also holds the packed token rows of the streaming gate/up
-  // (cap x H bf16) until the down kernels overwrite it
-  p->off_y = take((size_t)p->cap * p->H * 4);
+  // y rows (fp32; bf16 with fp8 weights) also hold the packed token rows of
+  // the streaming gate/up (cap x H bf16) until the down kernels overwrite them
+  p->off_y = take((size_t)p->cap * p->H * (p->w == MOE_FP8_E4M3 ? 2 : 4));
   p->total = o;
   return MOE_OK;
 }
@@ -315,7 +315,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   int32_t* nitems = at<int32_t>(ws, p.off_nitems);
   const bool gemm = p.big_thr != INT_MAX;
   void* h = at<void>(ws, p.off_h);
-  float* y = at<float>(ws, p.off_y);
+  void* y = at<void>(ws, p.off_y);
   const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
   const bool packed = desc->w_layout == MOE_LAYOUT_FRAG16;
 
@@ -372,7 +372,7 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   }
   {
     StageTimer tm(S_COMBINE, s);
-    if (moe::launch_combine(y, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+    if (moe::launch_combine(y, p.w == MOE_FP8_E4M3, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
                             p.act == MOE_BF16, s) != hipSuccess)
       return MOE_ERR_HIP;
   }

@@ -35,6 +35,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Four consecutive values of an expert output row y: fp32 (16 bytes), or
+// bf16 (8 bytes, round to nearest even) in fp8-weight layers.
+template <bool YB>
+__device__ __forceinline__ void store_y4(void* y, size_t idx, floatx4 v) {
+  if constexpr (YB)
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + idx) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  else
+    *reinterpret_cast<floatx4*>(static_cast<float*>(y) + idx) = v;
+}
+
 // 8 OCP e4m3fn codes (two dwords) -> 8 bf16, exact (every e4m3 value is a
 // bf16 value).  gfx950's scaled converter applies only the exponent of its
 // scale, so the scale here is 1 and block scales are applied elsewhere.

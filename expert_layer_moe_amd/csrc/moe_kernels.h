@@ -90,19 +90,20 @@ hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void*
 hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2, const float* s2,
                             const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
-                            const int32_t* seg_cnt, float* y, int H, int I, int max_tiles,
+                            const int32_t* seg_cnt, void* y, int H, int I, int max_tiles,
                             hipStream_t s);
 // Router GEMM: part[z][t][e] for K chunk z of ks (H % (128 ks) == 0); tiles
 // with no valid row are skipped (their partials are never read).
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s);
-// y[r, :] = W2_e h[r, :] for every sorted row r (fp32 rows; bf16 h in the
-// layout launch_gate_up writes).  packed: weights from launch_pack_weights.
+// y[r, :] = W2_e h[r, :] for every sorted row r (bf16 h in the layout
+// launch_gate_up writes; y rows fp32, bf16 with fp8 weights).  packed:
+// weights from launch_pack_weights.
 hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
-                       const int32_t* n_items, int max_items, float* y, int H, int I,
+                       const int32_t* n_items, int max_items, void* y, int H, int I,
                        int bm, int max_rows, hipStream_t s);
 // Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
 // K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
@@ -110,8 +111,9 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
 // columns 32 s + 8 g .. + 7.  `packed` kernels read this layout.
 hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t rows, int K,
                                hipStream_t s);
-// out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), rounded once.
-hipError_t launch_combine(const float* y, const int32_t* ids, const float* w,
+// out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), summed in fp32 and
+// rounded once; y rows fp32, or bf16 when y_bf16.
+hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s);
