@@ -72,36 +72,32 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const uint8_t* __restric
 // are fp32, or bf16 (YB) in fp8-weight layers.
 constexpr int kMaxSlots = 17;
 
-// 4 consecutive values of a y row as fp32; y is read once: non-temporal
-template <bool YB>
-__device__ __forceinline__ floatx4 load_y4(const void* y, size_t idx) {
-  if constexpr (YB) {
-    const u32x2 v =
-        __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(y) + idx));
-    return floatx4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
-                   __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
-  } else {
-    return __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(static_cast<const float*>(y) + idx));
-  }
-}
-
-template <int NV, bool YB>
-__global__ __launch_bounds__(256) void combine_kernel(
-    const void* __restrict__ y, const int32_t* __restrict__ ids,
-    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
-    int H, int k, int ns, void* __restrict__ out, int out_bf16) {
-  const int t = blockIdx.x;
-  const int kk = k + ns;
-  // the row's id, slot positions and weights are loaded together (a padding
-  // row's positions are stale and never used)
+// Slot positions and weights of row t (shared slot: weight 1), loaded
+// together with its id (a padding row's positions are stale and never used);
+// false for a padding row.
+__device__ __forceinline__ bool combine_slots(const int32_t* ids, const float* w,
+                                              const int32_t* slot_pos, int t, int k, int kk,
+                                              int (&pos)[kMaxSlots], float (&wt)[kMaxSlots]) {
   const bool valid = ids[(size_t)t * k] >= 0;
-  int pos[kMaxSlots];
-  float wt[kMaxSlots];
 #pragma unroll
   for (int j = 0; j < kMaxSlots; ++j) {
     pos[j] = j < kk ? slot_pos[(size_t)t * kk + j] : 0;
     wt[j] = j < k ? w[(size_t)t * k + j] : 1.f;
   }
+  return valid;
+}
+
+// fp32 y rows (y is read once: non-temporal loads)
+template <int NV>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const float* __restrict__ y, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
+    int H, int k, int ns, void* __restrict__ out, int out_bf16) {
+  const int t = blockIdx.x;
+  const int kk = k + ns;
+  int pos[kMaxSlots];
+  float wt[kMaxSlots];
+  const bool valid = combine_slots(ids, w, slot_pos, t, k, kk, pos, wt);
   // NV groups of 4 columns per thread, each group coalesced across the block;
   // all loads of a thread are issued before the sums
   int n[NV];
@@ -118,7 +114,8 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           if (n[v] < H) {
-            const floatx4 val = load_y4<YB>(y, (size_t)pos[j] * H + n[v]);
+            const floatx4 val = __builtin_nontemporal_load(
+                reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]));
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
           }
@@ -139,6 +136,45 @@ __global__ __launch_bounds__(256) void combine_kernel(
       *reinterpret_cast<floatx4*>(static_cast<float*>(out) + (size_t)t * H + n[v]) = acc[v];
     }
   }
+}
+
+// bf16 y rows (fp8-weight layers), bf16 out: 8 columns per thread, 16-byte
+// non-temporal y loads, all issued before the sums.
+__global__ __launch_bounds__(256) void combine_ybf_kernel(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int H, int k, int ns,
+    uint16_t* __restrict__ out) {
+  const int t = blockIdx.x, kk = k + ns;
+  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (n >= H) return;   // H % 8 == 0: a thread's 8 columns are all in range
+  int pos[kMaxSlots];
+  float wt[kMaxSlots];
+  const bool valid = combine_slots(ids, w, slot_pos, t, k, kk, pos, wt);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (valid) {
+    u32x4 val[kMaxSlots];
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j)
+      if (j < kk)
+        val[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(y + (size_t)pos[j] * H + n));
+#pragma unroll
+    for (int j = 0; j < kMaxSlots; ++j) {
+      if (j < kk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = fmaf(wt[j], __uint_as_float(val[j][q] << 16), acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wt[j], __uint_as_float(val[j][q] & 0xffff0000u), acc[2 * q + 1]);
+        }
+      }
+    }
+  }
+  u32x4 pk;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    pk[q] = (uint32_t)f32_to_bf16_bits(acc[2 * q]) | ((uint32_t)f32_to_bf16_bits(acc[2 * q + 1]) << 16);
+  *reinterpret_cast<u32x4*>(out + (size_t)t * H + n) = pk;
 }
 
 }  // namespace
@@ -174,17 +210,21 @@ hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const 
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s) {
-  if (H % 4 != 0) return hipErrorInvalidValue;
+  if (y_bf16) {
+    if (!out_bf16 || H % 8 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_ybf_kernel, dim3(T, (H + 2047) / 2048), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(y), ids, w, slot_pos, H, k, n_shared,
+                       static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
+  const float* yf = static_cast<const float*>(y);
   // two 4-column groups per thread once there are rows enough to fill the chip
-  const bool two = T >= 256;
-  const dim3 grid(T, two ? (H + 2047) / 2048 : (H + 1023) / 1024);
-  const int ob = out_bf16 ? 1 : 0;
-#define MOE_COMBINE(NV, YB)                                                                 \
-  hipLaunchKernelGGL((combine_kernel<NV, YB>), grid, dim3(256), 0, s, y, ids, w, slot_pos, T, \
-                     H, k, n_shared, out, ob)
-  if (y_bf16) { if (two) MOE_COMBINE(2, true); else MOE_COMBINE(1, true); }
-  else { if (two) MOE_COMBINE(2, false); else MOE_COMBINE(1, false); }
-#undef MOE_COMBINE
+  if (T >= 256)
+    hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, yf, ids,
+                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  else
+    hipLaunchKernelGGL(combine_kernel<1>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yf, ids,
+                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
   return hipGetLastError();
 }
 
