@@ -375,54 +375,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     else return wexp + (size_t)(n + m) * I + 32 * st + 8 * g;
   };
   auto tile_n0 = [&](int t) { return c_beg + (t * 4 + wave) * 64; };
-  for (int t = 0; t < kTallCPW; ++t) {
-    const int n0 = tile_n0(t);
-    if (n0 >= H) break;
-    float sk[KSTEPS / 4];   // fp8: scales of the tile's 128-row block, per 128-wide K block
+  // A half tile (32 output columns) at a time.  A half's W2 codes are all
+  // loaded before the previous half's y stores: the memory counter retires
+  // in order, so the MFMAs of a half never wait for those stores (loading
+  // only the first half of the K steps early, or a quarter, was slower).
+  using WCode = typename std::conditional<FP8, u32x2, u32x4>::type;
+  WCode wpre[KSTEPS][2];
+  float sk[KSTEPS / 4];   // fp8: their block scales (loaded with them)
+  auto w_code = [&](int nh, int st, int q) -> WCode {
+    // non-temporal: the tile's W2 columns are not read again by this block
+    if constexpr (FP8)
+      return __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st)));
+    else
+      return __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st)));
+  };
+  auto preload = [&](int nh) {
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) wpre[st][q] = w_code(nh, st, q);
     if constexpr (FP8) {
 #pragma unroll
-      for (int kb = 0; kb < KSTEPS / 4; ++kb) sk[kb] = sc[(n0 / 128) * (I / 128) + kb];
+      for (int kb = 0; kb < KSTEPS / 4; ++kb) sk[kb] = sc[(nh / 128) * (I / 128) + kb];
     }
-    // two 32-column halves: the y stores of the first overlap the MFMAs of
-    // the second
+  };
+  floatx4 acc[2][8];
+  auto half = [&]() {
 #pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      const int nh = n0 + 32 * hq;
-      floatx4 acc[2][8];
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < KSTEPS; ++st) {
+      bf16x8 wa[2];
 #pragma unroll
-      for (int st = 0; st < KSTEPS; ++st) {
-        bf16x8 wa[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          // non-temporal: the tile's W2 columns are not read again by this block
-          if constexpr (FP8)
-            wa[q] = fp8x8_scaled(__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-                                     static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st))),
-                                 sk[st / 4]);
-          else
-            wa[q] = as_bf16x8(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-                static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st))));
-        }
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
-#pragma unroll
-          for (int q = 0; q < 2; ++q) acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
-        }
+      for (int q = 0; q < 2; ++q) {
+        if constexpr (FP8) wa[q] = fp8x8_scaled(wpre[st][q], sk[st / 4]);
+        else wa[q] = as_bf16x8(wpre[st][q]);
       }
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const int row = mt * 16 + m;
-        if (row >= rows_here) continue;
-        const size_t yr = (size_t)(row_base + row) * H + nh + 4 * g;
+        const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) store_y4<FP8>(y, yr + 16 * q, acc[q][mt]);
+        for (int q = 0; q < 2; ++q) acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
       }
     }
+  };
+  auto store = [&](int nh) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const int row = mt * 16 + m;
+      if (row >= rows_here) continue;
+      const size_t yr = (size_t)(row_base + row) * H + nh + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) store_y4<FP8>(y, yr + 16 * q, acc[q][mt]);
+    }
+  };
+  if (tile_n0(0) >= H) return;
+  preload(tile_n0(0));
+  // scheduling barriers keep each half's loads, MFMAs and stores in their
+  // phase (hoisting the later loads spills registers)
+  for (int t = 0; t < kTallCPW; ++t) {
+    const int n0 = tile_n0(t);
+    half();
+    __builtin_amdgcn_sched_barrier(0);
+    preload(n0 + 32);
+    store(n0);
+    __builtin_amdgcn_sched_barrier(0);
+    half();
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = t + 1 < kTallCPW && tile_n0(t + 1) < H;
+    if (more) preload(tile_n0(t + 1));
+    store(n0 + 32);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more) break;
   }
 }
 
