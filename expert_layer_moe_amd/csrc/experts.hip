@@ -15,22 +15,22 @@
 #include "moe_kernels.h"
 
 #include <climits>
+#include <type_traits>
 
 namespace moe {
 namespace {
 
-// One lane's 8 weights of a fragment.  Each weight is read once per call, so
-// the loads are non-temporal: they need not displace the token and h tiles
-// that the blocks of a segment share through the caches.
-template <bool FP8>
+// One lane's 8 weights of a fragment; NT: a non-temporal load (for weights
+// that no other block of the launch reads).
+template <bool FP8, bool NT = false>
 __device__ __forceinline__ bf16x8 load_w8(const void* base, size_t elem_off) {
   if constexpr (FP8) {
-    const u32x2 v = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + elem_off));
+    const u32x2* p = reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + elem_off);
+    const u32x2 v = NT ? __builtin_nontemporal_load(p) : *p;
     return fp8x8_to_bf16x8(v[0], v[1]);
   } else {
-    return as_bf16x8(__builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem_off)));
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + elem_off);
+    return as_bf16x8(NT ? __builtin_nontemporal_load(p) : *p);
   }
 }
 
@@ -275,50 +275,58 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = 0; kk < I; kk += 32 * KU) {
-        bf16x8 b[KU][NT], a[KU][MT];
+      // W2 of a segment with one item is read by this block alone: non-temporal
+      // loads (measured faster); the items of a larger segment share it
+      // through L2 (normal loads measured faster)
+      auto k_loop = [&](auto nt_tag) {
+        constexpr bool kNT = decltype(nt_tag)::value;
+        for (int kk = 0; kk < I; kk += 32 * KU) {
+          bf16x8 b[KU][NT], a[KU][MT];
 #pragma unroll
-        for (int u = 0; u < KU; ++u)
+          for (int u = 0; u < KU; ++u)
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            b[u][nt] = load_w8<FP8>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
-#pragma unroll
-        for (int u = 0; u < KU; ++u)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
-        if constexpr (FP8) {
-          floatx4 p[MT][NT];
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < NT; ++nt)
+              b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
 #pragma unroll
           for (int u = 0; u < KU; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < te)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
-          const int kb = kk >> 7;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+          if constexpr (FP8) {
+            floatx4 p[MT][NT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
+            const int kb = kk >> 7;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
           }
-        } else {
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              if (t0 + mt < te)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
         }
-      }
+      };
+      if (cnt <= kStreamItemRows) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
       // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
