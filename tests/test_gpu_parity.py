@@ -361,3 +361,21 @@ def test_random_shapes_match_oracle(seed):
     if _gemm_capable(kw):
         with gemm_path():
             compare(inp, run_gpu(inp, layer))
+
+
+@pytest.mark.parametrize("w,I", [("bf16", 1024), ("fp8", 2048)])
+def test_streaming_units_beyond_the_capped_grid(w, I):
+    """Every segment on the streaming kernels with more gate/up work units
+    (128 items of 64 rows x 64 column groups = 8192) than their grid holds
+    (4096 blocks): blocks loop over the units."""
+    import expert_layer_moe_amd as moe
+    kw = dict(T=2048, H=256, E=32, k=4, I=I, w=w)
+    log(f"[case] streaming units beyond the grid: {kw}")
+    inp = random_small(seed=900 + I, **kw)
+    layer = device_layer(inp, packed=True)
+    moe.moe_set_path_thresholds(2**31 - 1, -1)   # no segment takes the GEMM
+    try:
+        gpu = run_gpu(inp, layer)
+    finally:
+        moe.moe_set_path_thresholds()
+    compare(inp, gpu)
