@@ -11,8 +11,11 @@
 //     LDS, epilogue h = SiLU(g) * u.
 //   down_tall_kernel (K = I <= 256): the 128 h rows resident in LDS, a sweep
 //     over output columns, weights as the A operand; y rows fp32.
-//   gemm_kernel (down for larger I, and the router): 128 rows x 256 weight
-//     rows, both operands staged through LDS per 64-wide K window.
+//   gemm_kernel (down for larger I, and the router of more than 128
+//     experts): 128 rows x 256 weight rows, both operands staged through LDS
+//     per 64-wide K window.
+//   router_tall_kernel (router of up to 128 experts): gate_up_tall_kernel's
+//     structure, R rows as the A operands.
 //
 // Fragment order everywhere: an LDS slot (16-row tile, step j) is 64 lanes x
 // 16 B, lane g*16 + r holding row r, K = 32 j + 8 g + (0..7) of the window.
@@ -623,6 +626,154 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+// Router logits of large batches with gate_up_tall_kernel's structure:
+// 128 consecutive token rows x 256 experts per block over one K chunk z of
+// ks.  Each wave owns 64 experts: two 32-row A operands of R (row-major,
+// straight from memory), while the x rows of each 64-wide K window come
+// through LDS as four 32-row B operands of the 32x32x16 MFMA.  Padding rows
+// are never read (zeros in LDS) and their partials are not written; a tile
+// with no valid row exits.  part[z][t][e] fp32.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void router_tall_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ valid,
+    const uint16_t* __restrict__ R, float* __restrict__ part, int T, int H, int E, int n_nt,
+    int n_tiles, int ks) {
+  __shared__ u32x4 xbuf[2][kASlots][kWave];   // 2 x 16 KB
+  const int lid = xcd_remap_g(blockIdx.x, gridDim.x);
+  if (lid >= n_tiles * n_nt * ks) return;
+  // tile-major: the K chunks and expert groups of one row tile are neighbours
+  const int tile = lid / (n_nt * ks), rest = lid - tile * (n_nt * ks);
+  const int nt = rest / ks, z = rest - nt * ks;
+  const int row_base = tile * kBM;
+  const int rows_here = min(kBM, T - row_base);
+  const int Kc = H / ks, kofs = z * Kc;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, hh = lane / 32, m = lane % 16;
+
+  // x staging: 4 x 16 B per thread per window (rows tid / 8 + 32 s)
+  const int asq = tid & 7;
+  uint32_t aoff[4];
+  int aslot[4];
+  bool aon[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int row = (tid >> 3) + 32 * s;
+    const int rr = min(row, rows_here - 1);
+    aon[s] = row < rows_here && (valid == nullptr || valid[row_base + rr] != 0);
+    aoff[s] = (uint32_t)((size_t)(row_base + rr) * H) + kofs + 8 * asq;
+    const int j = asq >> 2, l = (asq & 3) * 16 + (row & 15);
+    aslot[s] = ((row >> 4) * 2 + j) * kWave + swz(l, j);
+  }
+  if (!__syncthreads_or(aon[0] || aon[1] || aon[2] || aon[3])) return;
+  // R rows of this wave: experts e0 + 32 q + l32, K half hh of each step
+  const int e0 = nt * 256 + wave * 64;
+  bool ron[2];
+  size_t roff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = e0 + 32 * q + l32;
+    ron[q] = e < E;
+    roff[q] = (size_t)(ron[q] ? e : 0) * H + kofs + 8 * hh;
+  }
+  const bool wave_on = e0 < E;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  struct XStage { u32x4 a[4]; };
+  struct WStage { u32x4 c[2][2][2]; };   // [j][sub][q]
+  auto x_load = [&](XStage& S, int win) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      S.a[s] = aon[s] ? *reinterpret_cast<const u32x4*>(x + aoff[s] + (uint32_t)win * kKW) : zero;
+  };
+  auto x_store = [&](const XStage& S, int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) (&xbuf[buf][0][0])[aslot[s]] = S.a[s];
+  };
+  auto w_load = [&](WStage& W, int win) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          W.c[j][sub][q] = ron[q] ? ld16(R + roff[q] + (size_t)win * kKW + 32 * j + 16 * sub) : zero;
+  };
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][n][r] = 0.f;
+  auto compute = [&](const WStage& W, int buf) {
+    if (!wave_on) return;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const int xl = swz(16 * (2 * sub + hh) + m, j);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const bf16x8 xb =
+              __builtin_bit_cast(bf16x8, xbuf[buf][(2 * n + l32 / 16) * 2 + j][xl]);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) acc[q][n] = mfma32x32x16(as_bf16x8(W.c[j][sub][q]), xb, acc[q][n]);
+        }
+      }
+  };
+
+  // windows in pairs (Kc / 64 is even: H % (128 ks) == 0)
+  const int nwin = Kc / kKW, last = nwin - 1;
+  XStage xs0, xs1;
+  WStage ws0, ws1;
+  x_load(xs0, 0);
+  w_load(ws0, 0);
+  x_load(xs1, min(1, last));
+  w_load(ws1, min(1, last));
+  x_store(xs0, 0);
+  __syncthreads();
+  x_load(xs0, min(2, last));
+  for (int win = 0; win < nwin; win += 2) {
+    compute(ws0, 0);
+    w_load(ws0, min(win + 2, last));
+    x_store(xs1, 1);
+    __syncthreads();
+    x_load(xs1, min(win + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ws1, 1);
+    w_load(ws1, min(win + 3, last));
+    x_store(xs0, 0);
+    __syncthreads();
+    x_load(xs0, min(win + 4, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!wave_on) return;
+
+  // acc[q][n] lane (l32, hh) register r: expert e0 + 32 q + 8 (r / 4) + 4 hh +
+  // r % 4, token row 32 n + l32
+  float* dst = part + (size_t)z * T * E;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = 32 * n + l32;
+    if (row >= rows_here) continue;
+    if (valid != nullptr && valid[row_base + row] == 0) continue;
+    float* pr = dst + (size_t)(row_base + row) * E;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = e0 + 32 * q + 8 * c + 4 * hh;
+        if ((E & 3) == 0 && e + 3 < E) {
+          *reinterpret_cast<floatx4*>(pr + e) =
+              floatx4{acc[q][n][4 * c], acc[q][n][4 * c + 1], acc[q][n][4 * c + 2], acc[q][n][4 * c + 3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (e + i < E) pr[e + i] = acc[q][n][4 * c + i];
+        }
+      }
+  }
+}
+
 int round8g(int v) { return (v + 7) / 8 * 8; }
 
 template <int OP, bool FP8, bool PW>
@@ -707,8 +858,18 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s) {
   if (ks < 1 || H % (128 * ks) != 0) return hipErrorInvalidValue;
-  const int n_nt = (E + kBN - 1) / kBN;
   const int tiles = (T + kBM - 1) / kBM;
+  if (E <= 128) {
+    // gemm_kernel's 256-expert tiles would spend most of their MFMA work on
+    // absent experts; router_tall_kernel's waves own 64 experts each and the
+    // waves without any skip their MFMAs (gather_padded_e48, E = 48: 52 ->
+    // 34 us; with E = 256 it measured 71 us against gemm_kernel's 63 us)
+    dim3 grid(round8g(tiles * ks));
+    hipLaunchKernelGGL(router_tall_kernel, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       valid, static_cast<const uint16_t*>(R), part, T, H, E, 1, tiles, ks);
+    return hipGetLastError();
+  }
+  const int n_nt = (E + kBN - 1) / kBN;
   dim3 grid(round8g(tiles * n_nt * ks));
   hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false, false>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), R, nullptr, nullptr, nullptr, nullptr,
