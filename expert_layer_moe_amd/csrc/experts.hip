@@ -41,6 +41,26 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return (b & 7) * (nb >> 3) + (b >> 3);
 }
 
+// Unit u of the streaming kernels -> its segment (returned), column group
+// cg and item it within the segment (rows 64 it ..).  The item table lists
+// a segment's items together, so the segment's units form one range of
+// n_items(seg) x n_cols units, ordered column-group major: the items of a
+// segment that read the same weight columns are neighbours in dispatch
+// order (same XCD, at the same time), which lets them share those weights
+// through L2.
+__device__ __forceinline__ int unit_of_segment(int u, int n_cols, const int32_t* item_seg,
+                                               const int32_t* item_row0, const int32_t* seg_cnt,
+                                               int& cg, int& it) {
+  const int ig = u / n_cols;   // an item of the unit's segment
+  const int e = item_seg[ig];
+  const int ni = (seg_cnt[e] + kStreamItemRows - 1) / kStreamItemRows;
+  const int i0 = ig - item_row0[ig] / kStreamItemRows;   // the segment's first item
+  const int local = u - i0 * n_cols;
+  cg = local / ni;
+  it = local - cg * ni;
+  return e;
+}
+
 // The streaming kernels loop over n_live work units (known only on the
 // device) in rounds of gridDim.x (a multiple of 8): this block's unit of the
 // round that starts at u0, or -1.  A partial round is remapped over its
@@ -83,8 +103,8 @@ void gate_up_stream_kernel(
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
     const int lid = round_unit(u0, n_live);
     if (lid < 0) continue;
-    const int item = lid / n_cg, cgb = lid - item * n_cg;
-    const int e = item_seg[item];
+    int cgb, it;
+    const int e = unit_of_segment(lid, n_cg, item_seg, item_row0, seg_cnt, cgb, it);
     const int cnt = seg_cnt[e];
     const int row0 = seg_off[e];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -116,7 +136,7 @@ void gate_up_stream_kernel(
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // the item's 16-row tiles [tb, te) of the segment
-    const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+    const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
     for (int t0 = tb; t0 < te; t0 += MT) {
       // fragment-ordered token tiles (row0 is a multiple of 16); step s of
       // tile t at xa + 512 s
@@ -242,8 +262,8 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
     const int lid = round_unit(u0, n_live);
     if (lid < 0) continue;
-    const int item = lid / n_ng, ngb = lid - item * n_ng;
-    const int e = item_seg[item];
+    int ngb, it;
+    const int e = unit_of_segment(lid, n_ng, item_seg, item_row0, seg_cnt, ngb, it);
     const int cnt = seg_cnt[e];
     const int row0 = seg_off[e];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -262,7 +282,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // the item's 16-row tiles [tb, te) of the segment
-    const int tb = item_row0[item] >> 4, te = min((cnt + 15) >> 4, tb + MT);
+    const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
     for (int t0 = tb; t0 < te; t0 += MT) {
       // fragment-ordered h tiles (rows past cnt may hold anything: each token
       // row feeds only its own output column of the MFMA, never stored)
