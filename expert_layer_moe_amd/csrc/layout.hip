@@ -17,8 +17,10 @@ namespace {
 // of the memory system to the weight stream.  The down projection's input h
 // is written in the same order by the gate/up kernel.
 //
-// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15 (padding rows 0),
-// for the tiles of segments left to the streaming kernels.
+// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15, for the tiles of
+// segments left to the streaming kernels.  Padding rows are not written: an
+// MFMA keeps the rows of its token operand apart, so whatever they hold only
+// reaches output rows that are never stored.
 // grid = (cap / 16, chunks of kpc steps).
 __global__ __launch_bounds__(256) void pack_x_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
@@ -37,10 +39,10 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
   const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
   uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
   const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if (sid < 0) return;
 #pragma unroll 8
   for (int s = s0 + wave; s < s1; s += 4)
-    *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = sid >= 0 ? ld16(src + 32 * s) : zero;
+    *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = ld16(src + 32 * s);
 }
 
 // Weights in MFMA B-fragment order (the same tile / step / lane order as
