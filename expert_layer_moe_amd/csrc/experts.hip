@@ -345,7 +345,9 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
           }
         }
       };
-      if (cnt <= kStreamItemRows) k_loop(std::true_type{});
+      // (fragment-packed weights only: a row-major K step reads half of each
+      // 128-byte line, and the next step needs the line again)
+      if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
       else k_loop(std::false_type{});
       // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
 #pragma unroll

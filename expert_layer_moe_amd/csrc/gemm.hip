@@ -386,13 +386,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   WCode wpre[KSTEPS][2];
   float sk[KSTEPS / 4];   // fp8: their block scales (loaded with them)
   auto w_code = [&](int nh, int st, int q) -> WCode {
-    // non-temporal: the tile's W2 columns are not read again by this block
-    if constexpr (FP8)
-      return __builtin_nontemporal_load(
-          reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st)));
-    else
-      return __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st)));
+    // fragment-packed: non-temporal (each 512 B / 1 KB block is read once);
+    // row-major: a K step reads part of each 128-byte line, the next step
+    // the rest, so the line should stay cached
+    using P = const WCode*;
+    const P p = FP8 ? reinterpret_cast<P>(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st))
+                    : reinterpret_cast<P>(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st));
+    if constexpr (PW) return __builtin_nontemporal_load(p);
+    else return *p;
   };
   auto preload = [&](int nh) {
 #pragma unroll
