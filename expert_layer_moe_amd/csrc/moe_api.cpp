@@ -80,14 +80,17 @@ bool use_router_gemm(const moe_desc* d) {
 }
 
 // K split of the router logits (the top-k kernel sums the ks partials in a
-// fixed order).  The router GEMM's split depends on H only, so a row's logits
-// do not depend on the batch it comes in (a split batch reproduces the
-// unsplit one bit for bit).
+// fixed order).  The router GEMM's split depends on H and E only, so a
+// row's logits do not depend on the batch it comes in (a split batch
+// reproduces the unsplit one bit for bit).
 int choose_ks(const moe_desc* d) {
   if (d->act_dtype != MOE_BF16) return 1;
   if (use_router_gemm(d)) {
+    // more than 128 experts (the 256-expert GEMM, one block per CU): 4 K
+    // chunks measured faster than 8 (fewer partials for the top-k to sum)
+    const int max_ks = d->E > 128 ? 4 : 8;
     int ks = 1;
-    while (ks < 8 && d->H % (128 * ks * 2) == 0) ks *= 2;
+    while (ks < max_ks && d->H % (128 * ks * 2) == 0) ks *= 2;
     return ks;
   }
   const int ksteps = d->H / 32;
