@@ -135,6 +135,10 @@ SMALL = [
     dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),        # shared expert tiled
     # more than 8192 assignments: the span-parallel align
     dict(T=1200, H=256, E=64, k=8, I=128, n_shared=1, valid_frac=0.8),
+    # router of up to 128 experts on large batches: E not a multiple of 4
+    # (scalar partial stores), E across two waves, odd K windows per chunk
+    dict(T=1500, H=256, E=13, k=3, I=64, valid_frac=0.6),
+    dict(T=1030, H=384, E=100, k=5, I=128, n_shared=1),
 ]
 
 
