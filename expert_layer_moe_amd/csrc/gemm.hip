@@ -373,9 +373,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   const int c_beg = ch * 256 * kTallCPW;
   // W2 element offset of this lane's fragment of 16-column group n at step st
-  auto woff = [&](int n, int st) -> size_t {
-    if constexpr (PW) return wexp + ((size_t)(n / 16) * KSTEPS + st) * 512 + 8 * lane;
-    else return wexp + (size_t)(n + m) * I + 32 * st + 8 * g;
+  // Tile q of the half at nh: its A row j is output column
+  // nh + 8 (j / 4) + 4 q + j % 4, so that a lane's results of the two tiles
+  // are 8 consecutive columns of one row (one 16- or 32-byte y store).  Lane
+  // (g, m) loads row j = m: W2 row nh + dn, in 16-row block (nh + dn) / 16.
+  auto woff = [&](int nh, int q, int st) -> size_t {
+    const int dn = 8 * (m >> 2) + 4 * q + (m & 3);
+    if constexpr (PW)
+      return wexp + ((size_t)((nh + dn) / 16) * KSTEPS + st) * 512 + 8 * (16 * g + (dn & 15));
+    else return wexp + (size_t)(nh + dn) * I + 32 * st + 8 * g;
   };
   auto tile_n0 = [&](int t) { return c_beg + (t * 4 + wave) * 64; };
   // A half tile (32 output columns) at a time.  A half's W2 codes are all
@@ -390,8 +396,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // row-major: a K step reads part of each 128-byte line, the next step
     // the rest, so the line should stay cached
     using P = const WCode*;
-    const P p = FP8 ? reinterpret_cast<P>(static_cast<const uint8_t*>(w2) + woff(nh + 16 * q, st))
-                    : reinterpret_cast<P>(static_cast<const uint16_t*>(w2) + woff(nh + 16 * q, st));
+    const P p = FP8 ? reinterpret_cast<P>(static_cast<const uint8_t*>(w2) + woff(nh, q, st))
+                    : reinterpret_cast<P>(static_cast<const uint16_t*>(w2) + woff(nh, q, st));
     if constexpr (PW) return __builtin_nontemporal_load(p);
     else return *p;
   };
@@ -432,9 +438,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int mt = 0; mt < 8; ++mt) {
       const int row = mt * 16 + m;
       if (row >= rows_here) continue;
-      const size_t yr = (size_t)(row_base + row) * H + nh + 4 * g;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) store_y4<FP8>(y, yr + 16 * q, acc[q][mt]);
+      // columns nh + 8 g .. + 7: tile 0's four, then tile 1's
+      store_y8<FP8>(y, (size_t)(row_base + row) * H + nh + 8 * g, acc[0][mt], acc[1][mt]);
     }
   };
   if (tile_n0(0) >= H) return;

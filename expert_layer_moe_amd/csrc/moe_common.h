@@ -46,6 +46,19 @@ __device__ __forceinline__ void store_y4(void* y, size_t idx, floatx4 v) {
     *reinterpret_cast<floatx4*>(static_cast<float*>(y) + idx) = v;
 }
 
+// Eight consecutive values of y (a then b): fp32 (32 bytes) or bf16 (16).
+template <bool YB>
+__device__ __forceinline__ void store_y8(void* y, size_t idx, floatx4 a, floatx4 b) {
+  if constexpr (YB) {
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + idx) =
+        u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+              pack_bf16x2(b[2], b[3])};
+  } else {
+    *reinterpret_cast<floatx4*>(static_cast<float*>(y) + idx) = a;
+    *reinterpret_cast<floatx4*>(static_cast<float*>(y) + idx + 4) = b;
+  }
+}
+
 // 8 OCP e4m3fn codes (two dwords) -> 8 bf16, exact (every e4m3 value is a
 // bf16 value).  gfx950's scaled converter applies only the exponent of its
 // scale, so the scale here is 1 and block scales are applied elsewhere.
