@@ -439,10 +439,17 @@ void launch_gu(const GuArgs& a) {
                      a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg);
 }
 
+// up to 4 K steps per batch, 2 with fp8 weights or without a K split (the
+// limits keep every variant free of register spills)
 template <int KS, bool FP8, bool PW>
 void launch_gu_ku(int ku, const GuArgs& a) {
-  if (ku == 4) launch_gu<KS, 4, FP8, PW>(a);
-  else if (ku == 2) launch_gu<KS, 2, FP8, PW>(a);
+  if constexpr (!FP8 && KS > 1) {
+    if (ku == 4) {
+      launch_gu<KS, 4, FP8, PW>(a);
+      return;
+    }
+  }
+  if (ku >= 2) launch_gu<KS, 2, FP8, PW>(a);
   else launch_gu<KS, 1, FP8, PW>(a);
 }
 
