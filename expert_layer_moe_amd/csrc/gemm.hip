@@ -4,13 +4,15 @@
 // Instinct MI308X", results: prefill favours the part with more compute), so
 // a block works on a 128-row tile of one expert's sorted rows; fp8 weights
 // ("AMD Instinct MI355X: ATOM ...": block-scale GEMM; Step3 page: FP8
-// blockscale) are dequantised as value(q) * s in fp32 rounded to bf16.
+// blockscale) are dequantised as value(q) * s in fp32 rounded to bf16, except
+// in the fp8 down projection, which scales fp32 partial sums.
 //
 //   gate_up_tall_kernel: 128 rows x (128 gate + 128 up columns), 32x32x16
 //     MFMA; weights as the A operand straight from memory, x rows through
 //     LDS, epilogue h = SiLU(g) * u.
-//   down_tall_kernel (K = I <= 256): the 128 h rows resident in LDS, a sweep
-//     over output columns, weights as the A operand; y rows fp32.
+//   down_tall_kernel / down_tall_f8s_kernel (K = I <= 256, bf16 / fp8 W2): the
+//     128 h rows resident in LDS, a sweep over output columns, weights as the
+//     A operand; y rows fp32 (bf16 with fp8 weights).
 //   gemm_kernel (down for larger I, and the router of more than 128
 //     experts): 128 rows x 256 weight rows, both operands staged through LDS
 //     per 64-wide K window.
@@ -327,22 +329,21 @@ __device__ __forceinline__ bf16x8 fp8x8_scaled(u32x2 v, float s) {
   return __builtin_bit_cast(bf16x8, u32x4{out[0], out[1], out[2], out[3]});
 }
 
-// Down projection of the large segments for K = I = 32 KSTEPS (128 or 256):
-// a block keeps the h rows of one 128-row tile in LDS (MFMA fragment order,
-// loaded once) and sweeps a chunk of output columns.  Each wave takes 64
-// output columns at a time: their W2 fragments (the MFMA A operand, straight
-// from global memory; fp8 dequantised in registers as bf16(q s)) against the
-// resident h fragments (the B operand), so a lane ends with 4 consecutive
-// output columns of one row and stores them as 16 bytes.
+// Down projection of the large segments for K = I = 32 KSTEPS (128 or 256),
+// bf16 W2: a block keeps the h rows of one 128-row tile in LDS (MFMA fragment
+// order, loaded once) and sweeps a chunk of output columns.  Each wave takes
+// 64 output columns at a time: their W2 fragments (the MFMA A operand,
+// straight from global memory) against the resident h fragments (the B
+// operand), so a lane ends with 8 consecutive output columns of one row.
 // grid.x = round_up(max_tiles * n_chunks, 8); chunk = 256 * CPW columns.
 constexpr int kTallCPW = 4;   // 64-column tiles per wave per chunk
 
-template <int KSTEPS, bool FP8, bool PW>
+template <int KSTEPS, bool PW>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void down_tall_kernel(
-    const uint16_t* __restrict__ h, const void* __restrict__ w2, const float* __restrict__ s2,
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, void* __restrict__ y, int H, int n_chunks,
+    const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int n_chunks,
     int max_tiles) {
   constexpr int I = 32 * KSTEPS;
   __shared__ u32x4 hbuf[8 * KSTEPS][kWave];   // (row tile, step) slots, 1 KB each
@@ -366,8 +367,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int st = kp >> 2, gg = kp & 3;
     hbuf[(row >> 4) * KSTEPS + st][swz(gg * 16 + (row & 15), st & 1)] = v;
   }
-  // fp8: the W2 block scales of this expert ([H/128][I/128])
-  const float* sc = FP8 ? s2 + (size_t)e * (H / 128) * (I / 128) : nullptr;
   const size_t wexp = (size_t)e * H * I;   // first element of expert e's W2
   __syncthreads();
 
@@ -388,27 +387,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // loaded before the previous half's y stores: the memory counter retires
   // in order, so the MFMAs of a half never wait for those stores (loading
   // only the first half of the K steps early, or a quarter, was slower).
-  using WCode = typename std::conditional<FP8, u32x2, u32x4>::type;
-  WCode wpre[KSTEPS][2];
-  float sk[KSTEPS / 4];   // fp8: their block scales (loaded with them)
+  u32x4 wpre[KSTEPS][2];
   // normal (cached) loads: the tiles of one expert read the same W2 and
   // share it through L2 (non-temporal loads measured 510 against 420 us on
   // prefill_ub_fp8, fetching W2 from HBM once per tile)
-  auto w_code = [&](int nh, int st, int q) -> WCode {
-    using P = const WCode*;
-    const P p = FP8 ? reinterpret_cast<P>(static_cast<const uint8_t*>(w2) + woff(nh, q, st))
-                    : reinterpret_cast<P>(static_cast<const uint16_t*>(w2) + woff(nh, q, st));
-    return *p;
-  };
+  auto w_code = [&](int nh, int st, int q) -> u32x4 { return ld16(w2 + woff(nh, q, st)); };
   auto preload = [&](int nh) {
 #pragma unroll
     for (int st = 0; st < KSTEPS; ++st)
 #pragma unroll
       for (int q = 0; q < 2; ++q) wpre[st][q] = w_code(nh, st, q);
-    if constexpr (FP8) {
-#pragma unroll
-      for (int kb = 0; kb < KSTEPS / 4; ++kb) sk[kb] = sc[(nh / 128) * (I / 128) + kb];
-    }
   };
   floatx4 acc[2][8];
   auto half = [&]() {
@@ -420,10 +408,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int st = 0; st < KSTEPS; ++st) {
       bf16x8 wa[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if constexpr (FP8) wa[q] = fp8x8_scaled(wpre[st][q], sk[st / 4]);
-        else wa[q] = as_bf16x8(wpre[st][q]);
-      }
+      for (int q = 0; q < 2; ++q) wa[q] = as_bf16x8(wpre[st][q]);
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const bf16x8 hb = __builtin_bit_cast(bf16x8, hbuf[mt * KSTEPS + st][swz(lane, st & 1)]);
@@ -438,7 +423,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       const int row = mt * 16 + m;
       if (row >= rows_here) continue;
       // columns nh + 8 g .. + 7: tile 0's four, then tile 1's
-      store_y8<FP8>(y, (size_t)(row_base + row) * H + nh + 8 * g, acc[0][mt], acc[1][mt]);
+      store_y8<false>(y, (size_t)(row_base + row) * H + nh + 8 * g, acc[0][mt], acc[1][mt]);
     }
   };
   if (tile_n0(0) >= H) return;
@@ -459,6 +444,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     store(n0 + 32);
     __builtin_amdgcn_sched_barrier(0);
     if (!more) break;
+  }
+}
+
+// The same down projection for fp8 W2.  A wave takes a 64-column tile in two
+// halves of 64 rows (four 16-column A operands x four 16-row h operands per
+// 32-wide K step) that share the tile's W2 codes, so each h fragment read
+// from LDS feeds four MFMAs and each y row leaves as one 128-byte line (two
+// 64-byte halves written apart were written back to HBM twice about a third
+// of the time).  The second half loads the next tile's codes of each K step
+// once it has converted its own.  Codes become bf16 exactly; the 128x128
+// block scales multiply the fp32 accumulators instead (the first K block's
+// partial by s0 / s1 when the second begins, the sum by s1 at the end).
+// Tile q's A row j is output column 32 (q / 2) + 8 (j / 4) + 4 (q % 2) + j % 4,
+// so lane (g, m) ends with columns 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7
+// of its row.
+template <int KSTEPS, bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void down_tall_f8s_kernel(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ y, int H, int n_chunks,
+    int max_tiles) {
+  constexpr int I = 32 * KSTEPS;
+  constexpr int KB = I / 128;      // scale blocks along K
+  __shared__ u32x4 hbuf[8 * KSTEPS][kWave];
+  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
+  if (lid < 0) return;
+  const int mt_id = lid / n_chunks, ch = lid - mt_id * n_chunks;
+  const int e = tile_seg[mt_id];
+  const int r0 = tile_row0[mt_id];
+  const int row_base = seg_off[e] + r0;
+  const int rows_here = min(kBM, seg_cnt[e] - r0);
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int m = lane % 16, g = lane / 16;
+
+  const int c_beg = ch * 256 * kTallCPW;
+  auto tile_n0 = [&](int t) { return c_beg + (t * 4 + wave) * 64; };
+  // wave-uniform bases and 32-bit lane offsets (no 64-bit address per lane)
+  const uint8_t* wexp = w2 + (size_t)e * H * I;
+  const float* sc = s2 + (size_t)e * (H / 128) * KB;
+  auto w_code = [&](int n0, int st, int q) -> u32x2 {
+    const uint32_t row = n0 + 32 * (q >> 1) + 8 * (m >> 2) + 4 * (q & 1) + (m & 3);
+    uint32_t o;
+    if constexpr (PW) o = ((row >> 4) * KSTEPS + st) * 512 + 8 * (16 * g + (row & 15));
+    else o = row * I + 32 * st + 8 * g;
+    return ld8(wexp + o);
+  };
+  u32x2 wq[KSTEPS][4];
+  float sk[KB];
+  auto load_scales = [&](int n0) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sk[kb] = sc[(n0 / 128) * KB + kb];
+  };
+  const int nt_w = min(kTallCPW, max(0, (H - tile_n0(0) + 255) / 256));
+  if (nt_w > 0) {
+    load_scales(tile_n0(0));
+#pragma unroll
+    for (int st = 0; st < KSTEPS; ++st)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wq[st][q] = w_code(tile_n0(0), st, q);
+  }
+#pragma unroll
+  for (int i = 0; i < 128 * I / 8 / 256; ++i) {
+    const int P = i * 256 + tid;
+    const int row = P / (I / 8), kp = P - row * (I / 8);
+    const int rr = min(row, rows_here - 1);
+    const u32x4 v = ld16(h + (size_t)(row_base + rr) * I + 8 * kp);
+    const int st = kp >> 2, gg = kp & 3;
+    hbuf[(row >> 4) * KSTEPS + st][swz(gg * 16 + (row & 15), st & 1)] = v;
+  }
+  __syncthreads();
+
+  uint16_t* ytile = y + (size_t)row_base * H;
+  floatx4 acc[4][4];
+  for (int t = 0; t < nt_w; ++t) {
+    // the next tile's codes are loaded unconditionally (the last tile
+    // reloads its own from L2): conditional loads leave register copies at
+    // the loop's back edge that wait for every outstanding load and store
+    const int n0 = tile_n0(t), n1 = tile_n0(min(t + 1, nt_w - 1));
+    // acc = (A0 ratio + A1) fin = s0 A0 + s1 A1 for the two K blocks' partial
+    // sums A0, A1.  A zero s1, or one below 2^-64 |s0| (whose ratio could
+    // overflow), is replaced by s0 2^-64: an absolute change of at most
+    // 2^-63 |s0 A1|.
+    float ratio = 1.f, fin = sk[KB - 1];
+    if constexpr (KB == 2) {
+      const bool tiny = !(fabsf(sk[1]) >= fabsf(sk[0]) * 0x1p-64f) || sk[1] == 0.f;
+      ratio = tiny ? 0x1p64f : sk[0] / sk[1];
+      fin = tiny ? sk[0] * 0x1p-64f : sk[1];
+    }
+    load_scales(n1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[q][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KSTEPS; ++st) {
+        bf16x8 wa[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wa[q] = fp8x8_to_bf16x8(wq[st][q][0], wq[st][q][1]);
+        if (half == 1) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wq[st][q] = w_code(n1, st, q);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const bf16x8 hb =
+              __builtin_bit_cast(bf16x8, hbuf[(4 * half + mt) * KSTEPS + st][swz(lane, st & 1)]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (KB == 2 && st == KSTEPS / 2) acc[q][mt] *= ratio;
+            acc[q][mt] = mfma16x16x32(wa[q], hb, acc[q][mt]);
+          }
+        }
+        // one K step at a time (hoisting later steps' loads spills registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = (4 * half + mt) * 16 + m;
+        if (row >= rows_here) continue;
+        const uint32_t o = (uint32_t)row * H + n0 + 8 * g;
+        store_y8<true>(ytile, o, acc[0][mt] * fin, acc[1][mt] * fin);
+        store_y8<true>(ytile, o + 32, acc[2][mt] * fin, acc[3][mt] * fin);
+      }
+    }
   }
 }
 
@@ -840,17 +953,23 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
     const int n_chunks = (H + 256 * kTallCPW - 1) / (256 * kTallCPW);
     const dim3 grid(round8g(max_tiles * n_chunks));
     const uint16_t* hb = static_cast<const uint16_t*>(h);
-#define MOE_TALL(KS, F8, P)                                                                 \
-  hipLaunchKernelGGL((down_tall_kernel<KS, F8, P>), grid, dim3(256), 0, s, hb, w2, s2,      \
-                     tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, y, H, n_chunks, max_tiles)
+#define MOE_TALL(KS, P)                                                                     \
+  hipLaunchKernelGGL((down_tall_kernel<KS, P>), grid, dim3(256), 0, s, hb,                    \
+                     static_cast<const uint16_t*>(w2), tile_seg, tile_row0, n_tiles, seg_off,  \
+                     seg_cnt, static_cast<float*>(y), H, n_chunks, max_tiles)
+#define MOE_TALL8(KS, P)                                                                    \
+  hipLaunchKernelGGL((down_tall_f8s_kernel<KS, P>), grid, dim3(256), 0, s, hb,                \
+                     static_cast<const uint8_t*>(w2), s2, tile_seg, tile_row0, n_tiles, seg_off, \
+                     seg_cnt, static_cast<uint16_t*>(y), H, n_chunks, max_tiles)
     if (I == 128) {
-      if (fp8) { if (packed) MOE_TALL(4, true, true); else MOE_TALL(4, true, false); }
-      else { if (packed) MOE_TALL(4, false, true); else MOE_TALL(4, false, false); }
+      if (fp8) { if (packed) MOE_TALL8(4, true); else MOE_TALL8(4, false); }
+      else { if (packed) MOE_TALL(4, true); else MOE_TALL(4, false); }
     } else {
-      if (fp8) { if (packed) MOE_TALL(8, true, true); else MOE_TALL(8, true, false); }
-      else { if (packed) MOE_TALL(8, false, true); else MOE_TALL(8, false, false); }
+      if (fp8) { if (packed) MOE_TALL8(8, true); else MOE_TALL8(8, false); }
+      else { if (packed) MOE_TALL(8, true); else MOE_TALL(8, false); }
     }
 #undef MOE_TALL
+#undef MOE_TALL8
     return hipGetLastError();
   }
   const int n_nt = (H + kBN - 1) / kBN;

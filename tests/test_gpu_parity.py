@@ -209,6 +209,34 @@ def test_packed_weights_give_identical_output(kw, path):
     assert np.array_equal(a["out"], b["out"])
 
 
+@pytest.mark.parametrize("path", ["auto", "gemm"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_fp8_zero_and_tiny_block_scales(packed, path):
+    """W2 blocks whose first or second 128-wide K block has a zero scale, or a
+    second-block scale 1e-25 of the first: the block scales multiply fp32
+    partial sums in the kernels, and these cases take their edge paths."""
+    inp = random_small(T=400, H=512, E=4, k=2, I=256, w="fp8", seed=41)
+    s2 = inp.s2.clone()
+    E1, NB, _ = s2.shape
+    for e in range(E1):
+        for nb in range(NB):
+            c = (e + nb) % 4
+            if c == 0:
+                s2[e, nb, 1] = 0.0
+            elif c == 1:
+                s2[e, nb, 0] = 0.0
+            elif c == 2:
+                s2[e, nb, 1] = s2[e, nb, 0] * 1e-25
+    inp.s2 = s2
+    s13 = inp.s13.clone()
+    s13[0, :, 1] = 0.0
+    inp.s13 = s13
+    log(f"[case] fp8 zero/tiny scales packed={packed} path={path}")
+    with gemm_path() if path == "gemm" else contextlib.nullcontext():
+        gpu = run_gpu(inp, device_layer(inp, packed=packed))
+    compare(inp, gpu)
+
+
 def test_all_rows_padding_gives_zero_output():
     inp = random_small(T=40, H=256, E=8, k=2, I=64, seed=3)
     inp.valid = torch.zeros(40, dtype=torch.uint8)
