@@ -72,6 +72,43 @@ __device__ __forceinline__ bool beats(float av, int ae, float bv, int be) {
   return av > bv || (av == bv && ae < be);
 }
 
+// One step of a wave arg-max under (logit desc, id asc): take the pair held
+// by the lane that the DPP pattern CTRL names, if it beats this lane's.
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& bv, int& be) {
+  const float ov =
+      __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xf, 0xf, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xf, 0xf, false);
+  if (beats(ov, oe, bv, be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+// Wave-wide arg-max: within each 16-lane row by DPP (swap neighbours, swap
+// pairs, rotate by 4, rotate by 8 — every lane then holds its row's best),
+// then the four rows' bests read into scalars.  The order is total, so the
+// result does not depend on the reduction's shape.
+__device__ __forceinline__ void wave_argmax(float& bv, int& be) {
+  argmax_dpp<0xb1>(bv, be);    // quad_perm [1, 0, 3, 2]
+  argmax_dpp<0x4e>(bv, be);    // quad_perm [2, 3, 0, 1]
+  argmax_dpp<0x124>(bv, be);   // row_ror 4
+  argmax_dpp<0x128>(bv, be);   // row_ror 8
+  float rv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+  int re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int r = 16; r < kWave; r += 16) {
+    const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), r));
+    const int id = __builtin_amdgcn_readlane(be, r);
+    if (beats(v, id, rv, re)) {
+      rv = v;
+      re = id;
+    }
+  }
+  bv = rv;
+  be = re;
+}
+
 // One wave per row: expert e lives in lane e % 64, register e / 64.
 // k rounds of a wave-wide arg-max under (logit desc, id asc).
 constexpr int kMaxTopk = 16;
@@ -130,15 +167,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
           bv = v[i];
           be = lane + kWave * i;
         }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (beats(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
+      wave_argmax(bv, be);
       if (j == 0) top = bv;
       denom += expf(bv - top);
 #pragma unroll
