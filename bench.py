@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -37,11 +38,19 @@ KERNEL_SOURCES = {"gate_up": ("experts.hip", "moe_common.h"),
                   "gate_up_gemm": ("gemm.hip", "moe_common.h")}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed, so
+    that the hash follows the code and not its commentary."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(kernel: str = "gate_up") -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -450,12 +450,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // The same down projection for fp8 W2.  A wave takes a 64-column tile in two
 // halves of 64 rows (four 16-column A operands x four 16-row h operands per
 // 32-wide K step) that share the tile's W2 codes, so each h fragment read
-// from LDS feeds four MFMAs and each y row leaves as one 128-byte line (two
-// 64-byte halves written apart were written back to HBM twice about a third
-// of the time).  The second half loads the next tile's codes of each K step
-// once it has converted its own.  Codes become bf16 exactly; the 128x128
-// block scales multiply the fp32 accumulators instead (the first K block's
-// partial by s0 / s1 when the second begins, the sum by s1 at the end).
+// from LDS feeds four MFMAs and each y row leaves as one 128-byte line (a
+// line stored as two 64-byte halves some time apart reached HBM as two
+// writes about a third of the time, measured).  The second half loads the
+// next tile's codes of each K step once it has converted its own.  Codes
+// become bf16 exactly; the 128x128 block scales multiply the fp32
+// accumulators instead (the first K block's partial by s0 / s1 when the
+// second begins, the sum by s1 at the end).
 // Tile q's A row j is output column 32 (q / 2) + 8 (j / 4) + 4 (q % 2) + j % 4,
 // so lane (g, m) ends with columns 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7
 // of its row.
