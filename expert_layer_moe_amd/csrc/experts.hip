@@ -248,7 +248,7 @@ void gate_up_stream_kernel(
 // columns); each wave streams NT 16-row tiles of W2 (full K = I) once for
 // the item's (up to MT) 16-row tiles of h.  W2 is the MFMA's A operand, so
 // a lane ends with 4 consecutive output columns of one row, stored as one
-// 16-byte piece of the row's fp32 y.
+// piece of the row's y (16 bytes of fp32, or 8 of bf16 with fp8 weights).
 // Units: (item, column group), n_ng = ceil(H / (64 * NT)) per item (NT = 4).
 template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
