@@ -37,7 +37,6 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(
   const uint16_t* rp = R + (size_t)(ev ? e : 0) * H + 8 * g;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll 4
   for (int k = kb; k < ke; k += 32) {
     u32x4 a = rv ? *reinterpret_cast<const u32x4*>(xp + k) : zero;
     u32x4 b = ev ? *reinterpret_cast<const u32x4*>(rp + k) : zero;
