@@ -19,7 +19,8 @@ def _swapped_ffn(X, W13, W2):
 
 
 def _sigmoid_only(z):
-    return 1.0 / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):   # exp(-z) -> inf gives sigma = 0, as it should
+        return 1.0 / (1.0 + np.exp(-z))
 
 
 def _ties_high(l32_row, k):
