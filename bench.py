@@ -4,12 +4,20 @@
 
 A step is one moe_forward (router, top-k, align, gate/up GEMM + SiLU*mul,
 down GEMM, combine) over one batch of synthetic input already resident in
-HBM.  The default workload is the 48-expert top-3 decode share (256 gathered
-tokens, hidden 7168, inter 5120/8, bf16).  Prints one JSON line.
+HBM.  The headline workload is the 48-expert top-3 decode share (256
+gathered tokens, hidden 7168, inter 5120/8, bf16): its K timed steps give the
+top-level figures.  By default (--config all) the same run then measures
+every other workload with its own step count and nests the results under
+"workloads": the 256-expert decode share with a shared expert, the padded
+mixed-phase gather, the 8192-row prefill micro-batch with fp8 weights (the
+MFMA-bound half of the metric), the two micro-batches on two HIP streams,
+the unsplit 16384-row batch and the request-boundary split (7003 / 9381),
+and the tiny fp32 correctness layer.  Prints one JSON line.
 
-Extra modes (used for profiling runs, not by the driver):
-  --config NAME       another workload (tiny, decode_e48, decode_e256_shared,
-                      gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8)
+Other modes (profiling runs, not used by the driver):
+  --config NAME       only that workload (tiny, decode_e48, decode_e256_shared,
+                      gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8,
+                      prefill_unsplit, prefill_boundary_split)
   --no-cpu-baseline   skip the oracle timing
   --copy-calibrate    time a plain 1 GiB device copy (for counter scaling)
 """
@@ -20,6 +28,7 @@ import hashlib
 import re
 import json
 import os
+import platform
 import sys
 import time
 
@@ -31,6 +40,13 @@ PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "expert_layer_moe_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# the headline workload, and the others measured in the same run
+HEADLINE = "decode_e48"
+NESTED = ["decode_e256_shared", "gather_padded_e48", "prefill_ub_fp8", "prefill_pair_fp8",
+          "prefill_unsplit", "prefill_boundary_split", "tiny"]
+# two-call variants of the prefill workload: (first rows, second rows)
+PREFILL_SPLITS = {"prefill_pair_fp8": "midpoint", "prefill_boundary_split": "boundary"}
 
 
 # sources that define each timed kernel (counter records name this hash)
@@ -58,8 +74,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def compute_dtype(cfg) -> str:
+    """The arithmetic type of the expert GEMMs: fp32 FMA for fp32 layers,
+    bf16 MFMA (fp32 accumulation) otherwise; fp8 weights are converted to
+    bf16 on the way in."""
+    return "f32" if cfg.act == "f32" else "bf16"
+
+
 def algorithmic_work(cfg, ids, n_valid):
-    """Per-launch algorithmic bytes / flops of the expert kernels and of the
+    """Per-call algorithmic bytes / flops of the expert kernels and of the
     whole step: weights of touched experts only, valid rows only."""
     import numpy as np
     E, H, I, ns = cfg.E, cfg.H, cfg.I, cfg.n_shared
@@ -85,6 +108,24 @@ def algorithmic_work(cfg, ids, n_valid):
         step_bytes=w13 + w2 + x_bytes + out_bytes + r_bytes,
         step_flops=2.0 * n_valid * H * E + 2.0 * n_assign * 3 * H * I,
     )
+
+
+def host_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": affinity, "cpu_model": model,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def cpu_baseline(inp, min_s=10.0, max_s=30.0):
@@ -114,10 +155,12 @@ def cpu_baseline(inp, min_s=10.0, max_s=30.0):
         if (spent >= min_s and len(times) >= 3) or spent + times[-1] > max_s:
             break
     t = sorted(times)[len(times) // 2]
-    return {"value": round(sample.n_valid / t, 2), "unit": "tokens/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"{desc}; median of {len(times)} runs, {t:.2f} s each; "
-                      f"fp64 numpy/OpenBLAS oracle"}
+    res = {"value": round(sample.n_valid / t, 2), "unit": "tokens/s",
+           "cores": int(threads), "kind": "oracle",
+           "sample": f"{desc}; median of {len(times)} runs, {t:.2f} s each; "
+                     f"fp64 numpy oracle, its BLAS pool on {threads} threads"}
+    res.update(host_info())
+    return res
 
 
 def traffic_for(kernel: str, workload: str):
@@ -131,11 +174,261 @@ def traffic_for(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_steps(step, n):
+    """Milliseconds per step over n steps, between synchronisations."""
+    import torch
+    a, b = _events()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+class Workload:
+    """One workload made resident on the GPU: the layer (weights re-laid out
+    once at load time unless row_major), its inputs, outputs, workspaces and
+    the step that the timed region repeats."""
+
+    def __init__(self, name, row_major=False):
+        import torch
+        import expert_layer_moe_amd as moe
+        from workloads import get_config, make_inputs
+        from workloads.configs import boundary_split, midpoint_split
+
+        self.name = name
+        self.split = PREFILL_SPLITS.get(name)
+        whole = name in ("prefill_unsplit",) or self.split is not None
+        base = get_config("prefill_ub_fp8" if whole else name)
+        self.cfg = base.with_(T=base.full_T, ub=None) if whole else base
+        log(f"[bench] generating {name}")
+        self.inp = make_inputs(self.cfg)
+        self.packed = self.cfg.w != "f32" and not row_major
+        c = self.cfg
+        self.layer = moe.DeviceLayer(self.inp.router, self.inp.w13, self.inp.w2, c.k,
+                                     c.n_shared, self.inp.s13, self.inp.s2, packed=self.packed)
+        self.x = self.inp.x.cuda()
+        self.valid = None if self.inp.valid is None else self.inp.valid.cuda()
+        self.out = torch.empty_like(self.x)
+        self.n_valid = self.inp.n_valid
+        if self.split is None:
+            self.parts = None
+            self.ws = self.layer.workspace(c.T)
+        else:
+            a, b = (midpoint_split(c.T) if self.split == "midpoint"
+                    else boundary_split(list(base.requests)))
+            self.parts = []
+            for lo, n in ((0, a), (a, b)):
+                ws = torch.empty_like(self.layer.workspace(n))
+                self.parts.append((self.x[lo:lo + n], self.out[lo:lo + n], ws,
+                                   torch.cuda.Stream()))
+            self.rows = (a, b)
+        ids, _, _ = self.layer.route(self.x, self.valid)
+        torch.cuda.synchronize()
+        self.work = algorithmic_work(c, ids.cpu().numpy(), self.n_valid)
+
+    def step(self):
+        import torch
+        if self.parts is None:
+            self.layer.forward(self.x, self.valid, self.out, self.ws)
+            return
+        cur = torch.cuda.current_stream()
+        ev = torch.cuda.Event()
+        ev.record(cur)
+        for xx, oo, ww, s in self.parts:
+            s.wait_event(ev)
+            with torch.cuda.stream(s):
+                self.layer.forward(xx, None, oo, ww, stream=s)
+        for _, _, _, s in self.parts:
+            cur.wait_stream(s)
+
+    def free(self):
+        import torch
+        del self.layer, self.x, self.out, self.parts, self.inp
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def dominant_kernel(wl):
+    """Which gate/up kernel carries the work (weight-streaming or tiled GEMM),
+    from one untimed step with both bracketed."""
+    import torch
+    import expert_layer_moe_amd as moe
+    moe.moe_profile_enable(["gate_up", "gate_up_gemm"])
+    wl.step()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(None)
+    probe = moe.moe_profile_read()
+    return "gate_up_gemm" if probe["gate_up_gemm"][0] > probe["gate_up"][0] else "gate_up"
+
+
+def roofline(wl, dom, avg_s):
+    """The dominant kernel against its roofline: its arithmetic intensity
+    against the 312.5 flop/B bf16 ridge decides HBM or MFMA."""
+    w = wl.work
+    ai = w["gate_up_flops"] / w["gate_up_bytes"]
+    if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        ach = w["gate_up_flops"] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    else:
+        ach = w["gate_up_bytes"] / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4)}
+    roof["kernel"] = dom
+    roof["kernel_avg_us"] = round(avg_s * 1e6, 2)
+    # counters are stored per workload shape: a split or unsplit variant of
+    # the prefill batch has none of its own
+    roof["traffic"] = traffic_for(dom, wl.name) if wl.name == wl.cfg.name else None
+    return roof
+
+
+def step_fractions(wl, ms):
+    s = ms / 1e3
+    w = wl.work
+    return {"algorithmic_GB": round(w["step_bytes"] / 1e9, 4),
+            "algorithmic_GFLOP": round(w["step_flops"] / 1e9, 2),
+            "hbm_frac": round(w["step_bytes"] / s / 1e9 / PEAK_HBM_GBPS, 4),
+            "mfma_frac": round(w["step_flops"] / s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "touched_experts": w["touched_experts"]}
+
+
+def config_of(wl):
+    c = wl.cfg
+    cfg = {"workload": wl.name, "T": c.T, "valid_rows": wl.n_valid, "H": c.H, "E": c.E,
+           "topk": c.k, "I": c.I, "n_shared": c.n_shared, "weights": c.w,
+           "weight_layout": "frag16" if wl.packed else "row_major",
+           "two_streams": wl.parts is not None}
+    if wl.parts is not None:
+        cfg["calls_rows"] = list(wl.rows)
+    return cfg
+
+
+def stage_breakdown(wl, steps):
+    """Per-stage average microseconds, every stage bracketed by events (a
+    separate pass: the events perturb the timeline)."""
+    import torch
+    import expert_layer_moe_amd as moe
+    moe.moe_profile_enable("all")
+    for _ in range(steps):
+        wl.step()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(None)
+    st = moe.moe_profile_read()
+    return {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in st.items() if v[1]}
+
+
+def measure_nested(name, steps, warmup):
+    """Compact record of one non-headline workload."""
+    import torch
+    import expert_layer_moe_amd as moe
+    wl = Workload(name)
+    for _ in range(warmup):
+        wl.step()
+    ms = time_steps(wl.step, steps)
+    rec = {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.n_valid / (ms / 1e3), 1),
+           "steps": steps, "warmup": warmup, "dtype": compute_dtype(wl.cfg),
+           "config": config_of(wl)}
+    rec["step"] = step_fractions(wl, ms)
+    if wl.parts is None and wl.cfg.act != "f32":
+        dom = dominant_kernel(wl)
+        moe.moe_profile_enable([dom])
+        for _ in range(steps):
+            wl.step()
+        torch.cuda.synchronize()
+        moe.moe_profile_enable(None)
+        d_ms, d_n = moe.moe_profile_read()[dom]
+        rec["roofline"] = roofline(wl, dom, d_ms / max(d_n, 1) / 1e3)
+        rec["stages_us"] = stage_breakdown(wl, steps)
+    wl.free()
+    log(f"[bench] {name}: {rec['ms_per_step']} ms/step")
+    return rec
+
+
+def run_headline(args, name):
+    """The workload of the top-level figures: K timed steps (the dominant
+    kernel's launch bracketed by events in every fourth), then a breakdown
+    pass, an event-free pass and a HIP-graph pass."""
+    import torch
+    import expert_layer_moe_amd as moe
+
+    wl = Workload(name, row_major=args.row_major)
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    dom = dominant_kernel(wl) if wl.parts is None and wl.cfg.act != "f32" else None
+
+    # timed region: K steps; on the launch stream, a HIP event pair brackets
+    # the dominant kernel's launch (and nothing else) in every EVERY-th step,
+    # which samples its average duration while perturbing the timeline less
+    # than a pair around every launch
+    every = 4 if args.steps >= 8 else 1
+    t0, t1 = _events()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        if dom:
+            moe.moe_profile_enable([dom] if i % every == 0 else None)
+        wl.step()
+    t1.record()
+    torch.cuda.synchronize()
+    moe.moe_profile_enable(None)
+    ms_total = t0.elapsed_time(t1)
+    dom_rec = moe.moe_profile_read()
+    ms_step = ms_total / args.steps
+
+    res = {
+        "metric": METRIC, "value": round(wl.n_valid / (ms_step / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": compute_dtype(wl.cfg), "data": "synthetic",
+        "config": config_of(wl),
+    }
+    if args.gemm_min_rows is not None:
+        res["config"]["gemm_thresholds"] = [args.gemm_min_rows, args.gemm_min_tiles]
+    if dom:
+        g_ms, g_n = dom_rec[dom]
+        roof = roofline(wl, dom, g_ms / max(g_n, 1) / 1e3)
+        roof["launches_timed"] = int(g_n)
+        res["roofline"] = roof
+        res["stages_us"] = stage_breakdown(wl, args.steps)
+    ms_clean = time_steps(wl.step, args.steps)
+    res["step"] = step_fractions(wl, ms_step)
+    res["step"]["ms_per_step_without_events"] = round(ms_clean, 5)
+    res["event_overhead_pct"] = round(100.0 * (ms_step - ms_clean) / ms_clean, 2)
+
+    # HIP-graph pass: the step (both streams for a split batch) captured once
+    # and replayed K times; moe_forward only enqueues kernels, so it captures
+    res["graph_replay"] = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            wl.step()
+        g.replay()
+        ms_g = time_steps(g.replay, args.steps)
+        res["graph_replay"] = {"ms_per_step": round(ms_g, 5),
+                               "tokens_per_s": round(wl.n_valid / (ms_g / 1e3), 1)}
+        del g
+    res["source_sha"] = source_sha(dom or "gate_up")
+    res["cpu_baseline"] = None
+    if args.cpu_baseline and wl.parts is None:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = cpu_baseline(wl.inp)
+    wl.free()
+    return res
+
+
 def run(args):
     import torch
-    import numpy as np
     import expert_layer_moe_amd as moe
-    from workloads import get_config, make_inputs
 
     moe.load_library()
     if args.gemm_min_rows is not None:
@@ -149,182 +442,15 @@ def run(args):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n}), flush=True)
         return
-
-    pair = args.config == "prefill_pair_fp8"
-    cfg = get_config("prefill_ub_fp8" if pair else args.config)
-    log(f"[bench] generating {cfg.name}")
-    inp = make_inputs(cfg)
-    # expert weights re-laid out once at load time (not timed), as a serving
-    # deployment would; --row-major times the weights as handed over
-    packed = cfg.w != "f32" and not args.row_major
-    layer = moe.DeviceLayer(inp.router, inp.w13, inp.w2, cfg.k, cfg.n_shared,
-                            inp.s13, inp.s2, packed=packed)
-    x = inp.x.cuda()
-    valid = None if inp.valid is None else inp.valid.cuda()
-    out = torch.empty_like(x)
-    ws = layer.workspace(cfg.T)
-    streams = None
-    if pair:
-        ub1 = make_inputs(cfg.with_(ub=1))
-        x1 = ub1.x.cuda()
-        out1 = torch.empty_like(x1)
-        ws1 = torch.empty_like(ws)
-        streams = (torch.cuda.Stream(), torch.cuda.Stream())
-    def step():
-        if not pair:
-            layer.forward(x, valid, out, ws)
-            return
-        cur = torch.cuda.current_stream()
-        ev = torch.cuda.Event()
-        ev.record(cur)
-        for s, xx, oo, ww in ((streams[0], x, out, ws), (streams[1], x1, out1, ws1)):
-            s.wait_event(ev)
-            with torch.cuda.stream(s):
-                layer.forward(xx, None, oo, ww, stream=s)
-        for s in streams:
-            cur.wait_stream(s)
-
-    ids, _, _ = layer.route(x, valid)
-    torch.cuda.synchronize()
-    n_valid = inp.n_valid
-    work = algorithmic_work(cfg, ids.cpu().numpy(), n_valid)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # which gate/up kernel carries the work (weight-streaming or tiled GEMM):
-    # one untimed step with both bracketed
-    dom = "gate_up"
-    if not pair:
-        moe.moe_profile_enable(["gate_up", "gate_up_gemm"])
-        step()
-        torch.cuda.synchronize()
-        moe.moe_profile_enable(None)
-        probe = moe.moe_profile_read()
-        if probe["gate_up_gemm"][0] > probe["gate_up"][0]:
-            dom = "gate_up_gemm"
-
-    # timed region: K steps; on the launch stream, a HIP event pair brackets
-    # the dominant kernel's launch (and nothing else) in every EVERY-th step,
-    # which samples its average duration while perturbing the timeline less
-    # than a pair around every launch
-    every = 4 if args.steps >= 8 else 1
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        if not pair:
-            moe.moe_profile_enable([dom] if i % every == 0 else None)
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    moe.moe_profile_enable(None)
-    ms_total = t0.elapsed_time(t1)
-    dom_rec = moe.moe_profile_read()
-
-    # breakdown pass (not the headline): the same K steps with every stage
-    # bracketed, and once more with no events, to show the events' cost
-    stages = {}
-    ms_clean = ms_all = None
-    if not pair:
-        moe.moe_profile_enable("all")
-        a0 = torch.cuda.Event(enable_timing=True)
-        a1 = torch.cuda.Event(enable_timing=True)
-        a0.record()
-        for _ in range(args.steps):
-            step()
-        a1.record()
-        torch.cuda.synchronize()
-        moe.moe_profile_enable(None)
-        ms_all = a0.elapsed_time(a1)
-        stages = moe.moe_profile_read()
-    c0 = torch.cuda.Event(enable_timing=True)
-    c1 = torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(args.steps):
-        step()
-    c1.record()
-    torch.cuda.synchronize()
-    ms_clean = c0.elapsed_time(c1)
-
-    # HIP-graph pass: the step (both streams for the pair) captured once and
-    # replayed K times; moe_forward only enqueues kernels, so it captures
-    graph = None
-    if not args.no_graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        g.replay()
-        torch.cuda.synchronize()
-        g0 = torch.cuda.Event(enable_timing=True)
-        g1 = torch.cuda.Event(enable_timing=True)
-        g0.record()
-        for _ in range(args.steps):
-            g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        ms_g = g0.elapsed_time(g1) / args.steps
-        graph = {"ms_per_step": round(ms_g, 5),
-                 "tokens_per_s": round(n_valid * (2 if pair else 1) / (ms_g / 1e3), 1)}
-
-    ms_step = ms_total / args.steps
-    tokens_per_step = n_valid * (2 if pair else 1)
-    value = tokens_per_step / (ms_step / 1e3)
-    res = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": ("prefill_pair_fp8" if pair else cfg.name),
-                   "T": cfg.T * (2 if pair else 1), "valid_rows": tokens_per_step,
-                   "H": cfg.H, "E": cfg.E, "topk": cfg.k, "I": cfg.I,
-                   "n_shared": cfg.n_shared, "weights": cfg.w,
-                   "weight_layout": "frag16" if packed else "row_major",
-                   "two_streams": pair,
-                   "gemm_thresholds": (None if args.gemm_min_rows is None
-                                       else [args.gemm_min_rows, args.gemm_min_tiles])},
-    }
-    if not pair:
-        g_ms, g_n = dom_rec[dom]
-        avg_s = g_ms / max(g_n, 1) / 1e3
-        # bound by the kernel's arithmetic intensity against the ridge point
-        # (peak MFMA / peak HBM = 312.5 flop/B for bf16)
-        ai = work["gate_up_flops"] / work["gate_up_bytes"]
-        if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
-            ach = work["gate_up_flops"] / avg_s / 1e12
-            roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-        else:
-            ach = work["gate_up_bytes"] / avg_s / 1e9
-            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                    "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4)}
-        roof["kernel"] = dom
-        roof["kernel_avg_us"] = round(avg_s * 1e6, 2)
-        roof["launches_timed"] = int(g_n)
-        roof["traffic"] = traffic_for(dom, cfg.name)
-        res["roofline"] = roof
-        res["stages_us"] = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in stages.items()}
-        res["event_overhead_pct"] = {
-            "dominant_kernel_sampled": round(100.0 * (ms_total - ms_clean) / ms_clean, 2),
-            "every_stage": round(100.0 * (ms_all - ms_clean) / ms_clean, 2)}
-    step_s = ms_step / 1e3
-    res["step"] = {
-        "algorithmic_GB": round(work["step_bytes"] * (2 if pair else 1) / 1e9, 4),
-        "algorithmic_GFLOP": round(work["step_flops"] * (2 if pair else 1) / 1e9, 2),
-        "hbm_frac": round(work["step_bytes"] * (2 if pair else 1) / step_s / 1e9 / PEAK_HBM_GBPS, 4),
-        "mfma_frac": round(work["step_flops"] * (2 if pair else 1) / step_s / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "touched_experts": work["touched_experts"],
-        "ms_per_step_without_events": round(ms_clean / args.steps, 5),
-    }
-    res["graph_replay"] = graph
-    res["source_sha"] = source_sha(dom if not pair else "gate_up_gemm")
-    if args.cpu_baseline and not pair:
-        log("[bench] timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(inp)
+    if args.config == "all":
+        res = run_headline(args, HEADLINE)
+        nested = {}
+        for name in NESTED:
+            prefill = name.startswith("prefill")
+            nested[name] = measure_nested(name, steps=10 if prefill else 20, warmup=3)
+        res["workloads"] = nested
     else:
-        res["cpu_baseline"] = None
+        res = run_headline(args, args.config)
     print(json.dumps(res), flush=True)
 
 
@@ -333,7 +459,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="decode_e48")
+    ap.add_argument("--config", default="all",
+                    help="all (the headline workload, then every other one nested), "
+                         "or one workload name")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--copy-calibrate", action="store_true")
     ap.add_argument("--gemm-min-rows", type=int, default=None,
@@ -351,6 +479,9 @@ def main():
               "cross-GPU reduce_scatter is outside the measured path",
               file=sys.stderr)
         sys.exit(2)
+    valid = ["all", HEADLINE] + NESTED
+    if args.config not in valid:
+        ap.error(f"--config must be one of {valid}")
     run(args)
 
 

@@ -58,7 +58,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_size.restype = SZ
     lib.moe_route.argtypes = [D, P, P, P, I32, P, P, P, P, SZ, P]
     lib.moe_route.restype = ctypes.c_int
-    lib.moe_align.argtypes = [D, P, I32, I32, P, P, P, P, P]
+    lib.moe_align.argtypes = [D, P, I32, I32, P, P, P, P, P, SZ, P]
     lib.moe_align.restype = ctypes.c_int
     lib.moe_forward.argtypes = [D, P, P, P, P, P, I32, P, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
@@ -159,17 +159,21 @@ def moe_route(desc, x, valid_rows, router_w, topk, topk_ids, topk_w, logits=None
 
 
 def moe_align(desc, topk_ids, topk, block_m, sorted_ids, block_expert,
-              expert_offsets, n_post_padded, stream=None):
-    T, E = desc.T, desc.E
-    cap = T * topk + E * (block_m - 1)
+              expert_offsets, n_post_padded, workspace=None, stream=None):
+    T, E, ns = desc.T, desc.E, desc.n_shared
+    cap = T * (topk + ns) + (E + ns) * (block_m - 1)
     if sorted_ids.numel() < cap or block_expert.numel() < (cap + block_m - 1) // block_m:
         raise ValueError("sorted_ids / block_expert below the documented capacity")
+    if expert_offsets.numel() < E + ns + 1:
+        raise ValueError("expert_offsets holds E + n_shared + 1 entries")
     _check(load_library().moe_align(
         ctypes.byref(desc), _dev(topk_ids, "topk_ids", torch.int32, (T, topk)), topk,
         block_m, _dev(sorted_ids, "sorted_ids", torch.int32),
         _dev(block_expert, "block_expert", torch.int32),
-        _dev(expert_offsets, "expert_offsets", torch.int32, (E + 1,)),
-        _dev(n_post_padded, "n_post_padded", torch.int32, (1,)), _stream(stream)))
+        _dev(expert_offsets, "expert_offsets", torch.int32),
+        _dev(n_post_padded, "n_post_padded", torch.int32, (1,)),
+        _dev(workspace, "workspace", torch.uint8),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
 
 
 def moe_forward(desc, x, valid_rows, router_w, w13, w2, topk, out, workspace,

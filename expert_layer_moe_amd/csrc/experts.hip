@@ -520,7 +520,7 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   const int ku = pick_ku(H / ks);
   const int cgw = 4 / ks;
   const int n_cg = (I / 16 + cgw - 1) / cgw;
-  if (bm != 16 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
+  if (bm % 16 != 0 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
   GuArgs a{dim3(stream_grid(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
            seg_off, seg_cnt, item_seg, item_row0, n_items, static_cast<uint16_t*>(h), H, I,
            max_items, n_cg};

@@ -21,12 +21,13 @@ namespace {
 // segments left to the streaming kernels.  Padding rows are not written: an
 // MFMA keeps the rows of its token operand apart, so whatever they hold only
 // reaches output rows that are never stored.
-// grid = (cap / 16, chunks of kpc steps).
+// grid = (cap / 16, chunks of kpc steps); the sorted list's blocks (of the
+// segments' padding granularity) hold tiles_per_block 16-row tiles.
 __global__ __launch_bounds__(256) void pack_x_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ n_post,
     const int32_t* __restrict__ seg_cnt, int big_thr, const int32_t* __restrict__ gemm_tiles,
-    uint16_t* __restrict__ xp, int H, int k, int kpc) {
+    uint16_t* __restrict__ xp, int H, int k, int kpc, int tiles_per_block) {
   const int tile = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int m = lane % 16, g = lane / 16;
@@ -35,7 +36,9 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
   // loads matters in a kernel this small
   const int sid = sorted_ids[tile * 16 + m];
   if (tile * 16 >= *n_post) return;
-  if (gemm_tiles != nullptr && seg_cnt[block_expert[tile]] > big_thr && *gemm_tiles > 0) return;
+  if (gemm_tiles != nullptr && seg_cnt[block_expert[tile / tiles_per_block]] > big_thr &&
+      *gemm_tiles > 0)
+    return;
   const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
   uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
   const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
@@ -185,11 +188,12 @@ hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t
                          const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
                          const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
                          int max_rows, hipStream_t s) {
-  if (bm != 16 || H % 32 != 0) return hipErrorInvalidValue;
+  if (bm % 16 != 0 || H % 32 != 0 || max_rows % 16 != 0) return hipErrorInvalidValue;
   const int kpc = 32;   // MFMA steps per block
   hipLaunchKernelGGL(pack_x_kernel, dim3(max_rows / 16, (H / 32 + kpc - 1) / kpc), dim3(256), 0,
                      s, static_cast<const uint16_t*>(x), sorted_ids, block_expert, n_post,
-                     seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc);
+                     seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc,
+                     bm / 16);
   return hipGetLastError();
 }
 

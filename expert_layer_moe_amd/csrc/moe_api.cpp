@@ -43,13 +43,21 @@ constexpr int kBigSegRows = 128;
 std::atomic<int> g_gemm_min_rows{kBigSegRows};
 std::atomic<int> g_gemm_min_tiles{-1};   // -1: enough tiles to fill the chip
 
+// Padding granularity of the expert segments in the sorted row list: every
+// kernel works on 16-row MFMA tiles of a segment (the tiled GEMMs on 128-row
+// tiles inside it), so any multiple of 16 up to 256 gives the same result.
+bool valid_block_m(int bm) {
+  return bm == 0 || bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256;
+}
+int block_m_of(const moe_desc* d) { return d->block_m ? d->block_m : kDefaultBM; }
+
 int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
   if (d == nullptr) return MOE_ERR_INVALID_ARG;
   if (d->T < 1 || d->H < 1 || d->I < 1 || d->E < 1 || d->E > kMaxE)
     return MOE_ERR_INVALID_ARG;
   if (d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
   if (topk < 1 || topk > d->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
-  if (d->block_m != 0 && d->block_m != kDefaultBM) return MOE_ERR_UNSUPPORTED;
+  if (!valid_block_m(d->block_m)) return MOE_ERR_INVALID_ARG;
   if (d->w_layout != MOE_LAYOUT_ROW_MAJOR && d->w_layout != MOE_LAYOUT_FRAG16)
     return MOE_ERR_INVALID_ARG;
   if (d->w_layout == MOE_LAYOUT_FRAG16 && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
@@ -64,10 +72,14 @@ int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
     if (need_scales && (d->w13_scale == nullptr || d->w2_scale == nullptr))
       return MOE_ERR_INVALID_ARG;
   }
-  // sizes must fit the kernels' 32-bit row/element indexing of the row list
+  // sizes must fit the kernels' 32-bit row indexing of the sorted row list,
+  // and the 32-bit element offsets of h rows (sorted rows x I) in the tiled
+  // down GEMM
   const long long rows = (long long)d->T * (topk + d->n_shared) +
-                         (long long)(d->E + d->n_shared) * kDefaultBM;
+                         (long long)(d->E + d->n_shared) * block_m_of(d);
   if (rows > (1LL << 30) || (long long)d->T * d->H > (1LL << 40))
+    return MOE_ERR_UNSUPPORTED;
+  if ((unsigned long long)rows * (unsigned long long)d->I >= (1ULL << 32))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -105,7 +117,7 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   if (st != MOE_OK) return st;
   p->T = d->T; p->H = d->H; p->E = d->E; p->ns = d->n_shared; p->I = d->I;
   p->k = topk; p->act = d->act_dtype; p->w = d->w_dtype;
-  p->bm = kDefaultBM;
+  p->bm = block_m_of(d);
   p->ks = choose_ks(d);
   p->router_gemm = use_router_gemm(d);
   const int min_rows = g_gemm_min_rows.load();
@@ -273,18 +285,30 @@ int moe_route(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
 
 int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
               int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
-              int32_t* expert_offsets, int32_t* n_post_padded,
-              moe_stream_t stream) {
+              int32_t* expert_offsets, int32_t* n_post_padded, void* workspace,
+              size_t workspace_bytes, moe_stream_t stream) {
   if (desc == nullptr) return MOE_ERR_INVALID_ARG;
   if (desc->T < 1 || desc->E < 1 || desc->E > kMaxE) return MOE_ERR_INVALID_ARG;
+  if (desc->n_shared < 0 || desc->n_shared > 1) return MOE_ERR_INVALID_ARG;
   if (topk < 1 || topk > desc->E || topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (block_m < 1 || block_m > 256) return MOE_ERR_INVALID_ARG;
   if (!topk_ids || !sorted_ids || !block_expert || !expert_offsets || !n_post_padded)
     return MOE_ERR_INVALID_ARG;
-  if ((long long)desc->T * topk > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
-  if (moe::launch_align(topk_ids, desc->T, topk, desc->E, 0, block_m, sorted_ids,
+  const int ns = desc->n_shared;
+  if ((long long)desc->T * (topk + ns) + (long long)(desc->E + ns) * block_m > (1LL << 30))
+    return MOE_ERR_UNSUPPORTED;
+  // batches of more than 8192 assignments: the span-parallel kernels when a
+  // workspace is given, else one block does the whole list (same result)
+  int32_t* span = nullptr;
+  const int n_span = moe::align_spans(desc->T, topk, ns);
+  if (n_span > 0 && workspace != nullptr) {
+    if (workspace_bytes < (size_t)n_span * (desc->E + ns) * sizeof(int32_t))
+      return MOE_ERR_WORKSPACE;
+    span = static_cast<int32_t*>(workspace);
+  }
+  if (moe::launch_align(topk_ids, desc->T, topk, desc->E, ns, block_m, sorted_ids,
                         block_expert, expert_offsets, n_post_padded, nullptr, nullptr,
-                        INT_MAX, 0, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                        INT_MAX, 0, nullptr, nullptr, nullptr, span, nullptr, nullptr,
                         nullptr, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;

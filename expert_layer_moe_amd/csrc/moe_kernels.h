@@ -60,7 +60,7 @@ constexpr int kMaxGemmK = 16384;
 
 // bf16 streaming path: x rows of the sorted rows of the streaming kernels'
 // segments, packed in MFMA fragment order into xp (max_rows x H bf16, 16-row
-// tiles; padding rows 0).  bm must be 16.
+// tiles; padding rows 0).  bm (the segments' padding) is a multiple of 16.
 hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
                          const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
                          const int32_t* gemm_tiles, void* xp, int H, int k, int bm,

@@ -55,9 +55,9 @@ __global__ __launch_bounds__(256) void route_logits_bf16_kernel(
 __global__ __launch_bounds__(256) void route_logits_f32_kernel(
     const float* __restrict__ x, const uint8_t* __restrict__ valid,
     const float* __restrict__ R, float* __restrict__ part, int T, int H, int E) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * E) return;
-  const int t = idx / E, e = idx % E;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)T * E) return;
+  const int t = (int)(idx / E), e = (int)(idx % E);
   float acc = 0.f;
   if (valid == nullptr || valid[t] != 0) {
     const float* xp = x + (size_t)t * H;
@@ -197,8 +197,9 @@ hipError_t launch_route_logits(bool bf16, const void* x, const uint8_t* valid,
                        static_cast<const uint16_t*>(x), valid,
                        static_cast<const uint16_t*>(R), part, T, H, E, kchunk);
   } else {
-    const int n = T * E;
-    hipLaunchKernelGGL(route_logits_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
+    const size_t n = (size_t)T * E;
+    if ((n + 255) / 256 > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_logits_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(x), valid,
                        static_cast<const float*>(R), part, T, H, E);
   }

@@ -20,12 +20,13 @@ class DeviceLayer:
     router [E, H], w13 [E+ns, 2I, H], w2 [E+ns, H, I] (uint8 = fp8 e4m3fn codes
     with fp32 block scales s13 [E+ns, 2I/128, H/128], s2 [E+ns, H/128, I/128]).
     packed=True re-lays the expert weights out once with moe_pack_weights and
-    keeps only that copy (bf16 / fp8 weights).
+    keeps only that copy (bf16 / fp8 weights).  block_m: the descriptor's
+    segment padding (0 = library default).
     """
 
     def __init__(self, router, w13, w2, topk: int, n_shared: int = 0,
                  s13: Optional[torch.Tensor] = None, s2: Optional[torch.Tensor] = None,
-                 device="cuda", packed: bool = False):
+                 device="cuda", packed: bool = False, block_m: int = 0):
         self.router = router.to(device).contiguous()
         self.w13 = w13.to(device).contiguous()
         self.w2 = w2.to(device).contiguous()
@@ -44,6 +45,7 @@ class DeviceLayer:
             if self.s2 is None or tuple(self.s2.shape) != (ne, H // 128, I // 128):
                 raise ValueError("fp8 weights need s2 [E+ns, H/128, I/128]")
         self.device = device
+        self.block_m = block_m
         self._ws = {}
         self.layout = MOE_LAYOUT_ROW_MAJOR
         if packed:
@@ -52,7 +54,7 @@ class DeviceLayer:
 
     def desc(self, T: int):
         return make_desc(T, self.H, self.E, self.I, self.n_shared, self.act, self.wd,
-                         self.s13, self.s2, w_layout=self.layout)
+                         self.s13, self.s2, block_m=self.block_m, w_layout=self.layout)
 
     def workspace(self, T: int) -> torch.Tensor:
         if T not in self._ws:

@@ -74,7 +74,12 @@ enum moe_weight_layout { MOE_LAYOUT_ROW_MAJOR = 0, MOE_LAYOUT_FRAG16 = 1 };
  *             MOE_FP8_E4M3 (both with BF16 activations)
  *   w13_scale fp8 only: fp32 [E+n_shared, 2I/128, H/128] block scales
  *   w2_scale  fp8 only: fp32 [E+n_shared, H/128, I/128] block scales
- *   block_m   GEMM block rows used inside moe_forward; 0 = library default
+ *   block_m   padding granularity of the expert segments in moe_forward's
+ *             sorted row list: 0 (library default, 16), 16, 32, 64, 128 or
+ *             256 (else MOE_ERR_INVALID_ARG).  The kernels work on 16-row MFMA
+ *             tiles of a segment and the tiled GEMMs on 128-row tiles inside
+ *             it, so every accepted value gives the same output bits; larger
+ *             values only cost workspace
  *   w_layout  MOE_LAYOUT_ROW_MAJOR: w13 / w2 as documented at moe_forward;
  *             MOE_LAYOUT_FRAG16: the same weights re-laid out by
  *             moe_pack_weights (BF16 activations only)
@@ -113,20 +118,33 @@ int moe_route(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
 /* Align: stable counting sort of the flat assignments a = t*topk + j by
  * expert id.  Expert segments in ascending expert order, ascending a inside a
  * segment; each segment padded with -1 to a multiple of block_m; experts with
- * no assignment get no block; ids of -1 are skipped.
+ * no assignment get no block; ids of -1 are skipped.  With desc->n_shared = 1
+ * the shared expert is one more segment (expert E, after the routed ones)
+ * holding every row t with topk_ids[t][0] >= 0, entered as t*topk; so in
+ * every segment, entry / topk is the token row.  Only desc->T, E and
+ * n_shared are read.
  *   topk_ids        [T, topk] int32 (values in [0, E) or -1)
  *   block_m         1..256
- *   sorted_ids      out, capacity >= T*topk + E*(block_m-1) int32
- *   block_expert    out, capacity >= that / block_m: expert of each block
- *   expert_offsets  out [E+1] int32: padded segment starts, [E] = total
+ *   sorted_ids      out, capacity >= T*(topk+n_shared) + (E+n_shared)*(block_m-1)
+ *   block_expert    out, capacity >= that / block_m: segment of each block
+ *   expert_offsets  out [E+n_shared+1] int32: padded segment starts, last = total
  *   n_post_padded   out [1] int32: total padded length
+ *   workspace       NULL, or >= 4*ceil(T*(topk+n_shared)/4096)*(E+n_shared)
+ *                   bytes (moe_workspace_size(desc, topk) always suffices):
+ *                   batches of more than 8192 assignments then run the count /
+ *                   scan / scatter over 4096-assignment spans in parallel;
+ *                   with NULL one workgroup sorts the whole list.  Both give
+ *                   the same bits.  MOE_ERR_WORKSPACE if workspace_bytes is
+ *                   too small.
  * Only the first n_post_padded / n_post_padded/block_m entries are written.
  * (Per-expert block granularity: "[SGLang] Single Batch Overlap for MoE
- * models", combine signal section, one signal per 64-token block.) */
+ * models", combine signal section, one signal per 64-token block; padding
+ * rows of the gathered batch carry no assignment: "DP Attention and TBO for
+ * DeepSeek-V4 on MI355X", PrefillDelayer section.) */
 int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
               int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
-              int32_t* expert_offsets, int32_t* n_post_padded,
-              moe_stream_t stream);
+              int32_t* expert_offsets, int32_t* n_post_padded, void* workspace,
+              size_t workspace_bytes, moe_stream_t stream);
 
 /* The whole layer: route -> align -> gate/up GEMM with SiLU(g)*u -> down GEMM
  * -> combine out[t] = sum_j w[t,j] * y_{ids[t,j]}(x_t) (+ shared experts with

@@ -64,7 +64,18 @@ def test_status_strings():
     (dict(act_dtype=moe.MOE_F32), 3, -2),
     (dict(w_dtype=moe.MOE_FP8_E4M3), 3, -1),     # fp8 without scales
     (dict(w_dtype=moe.MOE_FP8_E4M3, I=704, w13_scale=FAKE, w2_scale=FAKE), 3, -2),
-    (dict(block_m=48), 3, -2),
+    (dict(block_m=48), 3, -1),
+    (dict(block_m=8), 3, -1),
+    (dict(block_m=16), 3, 0),
+    (dict(block_m=32), 3, 0),
+    (dict(block_m=64), 3, 0),
+    (dict(block_m=128), 3, 0),
+    (dict(block_m=256), 3, 0),
+    # sorted rows x I at 2^32 and above: past the tiled down GEMM's 32-bit
+    # element offsets of h rows
+    (dict(T=1 << 20, E=48, I=1024), 8, -2),
+    (dict(T=1 << 19, E=48, I=1024), 8, -2),
+    (dict(T=1 << 19, E=48, I=512), 8, 0),
     (dict(w_layout=moe.MOE_LAYOUT_FRAG16), 3, 0),
     (dict(w_layout=2), 3, -1),
     (dict(w_layout=moe.MOE_LAYOUT_FRAG16, H=256, I=64, act_dtype=moe.MOE_F32,
@@ -101,10 +112,20 @@ def test_null_pointers_rejected():
 def test_align_validation():
     lib = moe.load_library()
     d = _d()
-    assert lib.moe_align(ctypes.byref(d), FAKE, 3, 0, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert lib.moe_align(ctypes.byref(d), FAKE, 3, 257, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert lib.moe_align(ctypes.byref(d), FAKE, 49, 32, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert lib.moe_align(ctypes.byref(d), None, 3, 32, FAKE, FAKE, FAKE, FAKE, None) == -1
+    A = lambda desc, ids, k, bm, ws=None, nbytes=0: lib.moe_align(
+        ctypes.byref(desc) if desc is not None else None, ids, k, bm, FAKE, FAKE, FAKE, FAKE,
+        ws, nbytes, None)
+    assert A(d, FAKE, 3, 0) == -1
+    assert A(d, FAKE, 3, 257) == -1
+    assert A(d, FAKE, 49, 32) == -1
+    assert A(d, None, 3, 32) == -1
+    assert A(None, FAKE, 3, 32) == -1
+    assert A(_d(n_shared=2), FAKE, 3, 32) == -1
+    # more than 8192 assignments with a workspace below 4 ceil(n / 4096) (E + ns)
+    # bytes: rejected before any launch
+    big = _d(T=4096, E=48, n_shared=1)
+    need = 4 * ((4096 * 4 + 4095) // 4096) * 49
+    assert A(big, FAKE, 3, 16, FAKE, need - 1) == -3
 
 
 def test_pack_weights_validation():

@@ -34,3 +34,38 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_dtype_follows_the_workload():
+    from workloads import get_config
+    assert bench.compute_dtype(get_config("tiny")) == "f32"
+    assert bench.compute_dtype(get_config("decode_e48")) == "bf16"
+    # fp8 weights are converted to bf16 for bf16 MFMA
+    assert bench.compute_dtype(get_config("prefill_ub_fp8")) == "bf16"
+
+
+def test_host_info_names_the_cpu():
+    info = bench.host_info()
+    assert info["nproc"] >= 1 and info["usable_cpus"] >= 1
+    assert isinstance(info["cpu_model"], str)
+
+
+def test_unknown_config_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "nope"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=120)
+    assert r.returncode == 2 and r.stdout == ""
+
+
+def test_algorithmic_work_counts_touched_experts_and_valid_rows():
+    """decode_e48-shaped counts by hand: 2 touched experts of I = 640, H = 7168,
+    bf16, 3 valid rows of 5, top-3."""
+    import numpy as np
+    from workloads import get_config
+    cfg = get_config("decode_e48").with_(T=5)
+    ids = np.array([[0, 5, 5], [5, 0, 0], [-1, -1, -1], [0, 0, 5], [-1, -1, -1]])
+    w = bench.algorithmic_work(cfg, ids, 3)
+    H, I = 7168, 640
+    assert w["touched_experts"] == 2
+    assert w["gate_up_bytes"] == 2 * 2 * I * H * 2 + 3 * H * 2
+    assert w["gate_up_flops"] == 2.0 * 3 * 3 * H * 2 * I
+    assert w["step_bytes"] == 2 * 3 * I * H * 2 + 3 * H * 2 + 5 * H * 2 + 48 * H * 2

@@ -378,3 +378,83 @@ def test_admissible_sets():
     assert oracle.admissible_sets(l, 2, 0.0) == [(0, 2)]
     sets = oracle.admissible_sets(l, 2, 0.05)
     assert sets == [(0, 1), (0, 2), (0, 4)]
+
+
+def _brute_admissible(l, k, delta):
+    """Every k-subset S with min over S >= max over the rest - delta, by
+    enumerating all k-subsets (the definition, no shortcut)."""
+    E = len(l)
+    res = []
+    for S in itertools.combinations(range(E), k):
+        rest = [l[u] for u in range(E) if u not in S]
+        if not rest or min(l[s] for s in S) >= max(rest) - delta:
+            res.append(tuple(S))
+    return res
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_admissible_sets_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(2, 9))
+    k = int(rng.integers(1, E + 1))
+    # coarse values: many exact and near ties
+    l = rng.integers(-3, 4, size=E) + rng.choice([0.0, 1e-7, -1e-7, 0.5], size=E)
+    delta = float(rng.choice([0.0, 1e-6, 0.3, 0.6]))
+    assert oracle.admissible_sets(l, k, delta) == _brute_admissible(l.tolist(), k, delta)
+
+
+def test_tie_threshold_hand_worked():
+    g = _load("near_tie_example.json")["threshold"]
+    d = oracle.tie_threshold(np.array(g["x"], dtype=np.float64), np.array(g["R"], dtype=np.float64))
+    assert d.tolist() == [v * 2.0 ** -20 for v in g["expected_delta_in_units_of_2^-20"]]
+
+
+def test_near_tie_rows_constructed_gaps():
+    g = _load("near_tie_example.json")["near_tie_rows"]
+    rows = oracle.near_tie_rows(np.array(g["logits"]), g["k"], np.array(g["delta"]),
+                                np.array(g["valid"], dtype=bool))
+    assert rows.tolist() == g["expected_rows"]
+
+
+def _alt_layer():
+    g = _load("near_tie_example.json")["alternate_set_layer"]
+    L = math.log(3.0)
+    w13 = np.concatenate([np.array(g["gate_rows_in_units_of_L"]) * L, np.array(g["up_rows"])],
+                         axis=1)
+    inp = _inputs_from_arrays(np.array(g["x"], dtype=np.float64),
+                              np.array(g["router_in_units_of_L"]) * L, w13, np.array(g["w2"]),
+                              g["k"], n_shared=g["n_shared"])
+    return g, L, inp
+
+
+def test_alternate_set_row_hand_worked():
+    """A row with an exact tie for its last slot: the oracle's own routing,
+    its admissible sets, and the layer output of that row under the other
+    admissible set (the shared expert still added with weight 1)."""
+    g, L, inp = _alt_layer()
+    out, r = oracle.moe_forward(inp, return_routing=True)
+    assert r["ids"].tolist() == g["expected_ids"]
+    assert np.allclose(out, np.array(g["expected_out_in_units_of_L"]) * L, rtol=0, atol=1e-14)
+    t = g["alternate_row"]
+    delta = oracle.tie_threshold(r["x64"], r["R64"])
+    adm = oracle.admissible_sets(r["logits"][t], g["k"], delta[t])
+    assert adm == [tuple(s) for s in g["expected_admissible_sets_row1"]]
+    assert oracle.near_tie_rows(r["logits"], g["k"], delta).tolist() == [0, 1]
+    alt = oracle.forward_rows_with_sets(inp, r["x64"], r["logits"], [t], [g["alternate_set"]])
+    assert np.allclose(alt[0], np.array(g["expected_alternate_out_in_units_of_L"]) * L,
+                       rtol=0, atol=1e-14)
+    own = oracle.forward_rows_with_sets(inp, r["x64"], r["logits"], [0, 1], r["ids"].tolist())
+    assert np.allclose(own, out, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("n_shared,w", [(0, "bf16"), (1, "bf16"), (1, "fp8")])
+def test_forward_rows_with_own_sets_reproduce_the_layer(n_shared, w):
+    """Routing each valid row to the oracle's own expert set reproduces the
+    layer's rows (fp64, so only the matmul grouping differs)."""
+    inp = random_small(T=30, H=256, E=12, k=3, I=128, n_shared=n_shared, w=w, seed=53,
+                       valid_frac=0.7)
+    out, r = oracle.moe_forward(inp, return_routing=True)
+    rows = np.nonzero(inp.valid.numpy())[0].tolist()
+    sets = [r["ids"][t].tolist() for t in rows]
+    got = oracle.forward_rows_with_sets(inp, r["x64"], r["logits"], rows, sets)
+    assert np.allclose(got, out[rows], rtol=1e-12, atol=1e-15)

@@ -60,6 +60,56 @@ def _transposed_scales(codes, scales, block=128):
     return q * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
 
 
+def _delta_wrong_exponent(x64, R64):
+    rn = np.sqrt((R64 * R64).sum(axis=1)).max()
+    return (2.0 ** -10) * np.sqrt((x64 * x64).sum(axis=1)) * rn
+
+
+def _delta_l1_rows(x64, R64):
+    rn = np.sqrt((R64 * R64).sum(axis=1)).max()
+    return (2.0 ** -20) * np.abs(x64).sum(axis=1) * rn
+
+
+def _delta_min_router_norm(x64, R64):
+    rn = np.sqrt((R64 * R64).sum(axis=1)).min()
+    return (2.0 ** -20) * np.sqrt((x64 * x64).sum(axis=1)) * rn
+
+
+def _ties_top_k_only(logits64, k, delta, valid=None):
+    T, E = logits64.shape
+    out = []
+    for t in range(T):
+        if valid is not None and not valid[t]:
+            continue
+        srt = np.sort(logits64[t])[::-1][:k]          # misses the (k+1)-th
+        if np.any(np.diff(-srt) < delta[t]):
+            out.append(t)
+    return np.asarray(out, dtype=np.int64)
+
+
+def _ties_ignore_valid(logits64, k, delta, valid=None):
+    return _ORIG_NEAR(logits64, k, delta, None)
+
+
+def _sets_without_shared(inp, x64, logits64, rows, sets):
+    cfg = inp.cfg
+    res = np.zeros((len(rows), cfg.H))
+    for i, (t, s) in enumerate(zip(rows, sets)):
+        s = list(s)
+        for e, c in zip(s, mo.topk_weights(logits64[t, s])):
+            W13, W2 = mo.expert_weights_f64(inp, e)
+            res[i] += c * mo.expert_ffn(x64[t:t + 1], W13, W2)[0]
+    return res
+
+
+def _sets_wrong_row(inp, x64, logits64, rows, sets):
+    # the i-th listed row's output computed from x row i instead of row rows[i]
+    return _ORIG_SETS(inp, x64, logits64, list(range(len(rows))), sets)
+
+
+_ORIG_NEAR = mo.near_tie_rows
+_ORIG_SETS = mo.forward_rows_with_sets
+
 MUTANTS = [
     ("expert_ffn", _swapped_ffn, [pins.test_hand_worked_layer_example]),
     ("silu", _sigmoid_only, [pins.test_silu_closed_forms]),
@@ -68,10 +118,17 @@ MUTANTS = [
     ("align", _unstable_align, [lambda: pins.test_align_matches_comparison_sort(2, 16)]),
     ("e4m3fn_decode", _bad_bias_decode, [pins.test_fp8_table_matches_torch_cast_all_codes]),
     ("dequant_block_scaled", _transposed_scales, [pins.test_fp8_golden_codes_and_block_scales]),
+    ("tie_threshold", _delta_wrong_exponent, [pins.test_tie_threshold_hand_worked]),
+    ("tie_threshold", _delta_l1_rows, [pins.test_tie_threshold_hand_worked]),
+    ("tie_threshold", _delta_min_router_norm, [pins.test_tie_threshold_hand_worked]),
+    ("near_tie_rows", _ties_top_k_only, [pins.test_near_tie_rows_constructed_gaps]),
+    ("near_tie_rows", _ties_ignore_valid, [pins.test_near_tie_rows_constructed_gaps]),
+    ("forward_rows_with_sets", _sets_without_shared, [pins.test_alternate_set_row_hand_worked]),
+    ("forward_rows_with_sets", _sets_wrong_row, [pins.test_alternate_set_row_hand_worked]),
 ]
 
 
-@pytest.mark.parametrize("name,fn,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
+@pytest.mark.parametrize("name,fn,checks", MUTANTS, ids=[m[1].__name__ for m in MUTANTS])
 def test_planted_mistake_is_caught(monkeypatch, name, fn, checks):
     _patch(monkeypatch, name, fn)
     for check in checks:
