@@ -22,6 +22,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
+           "moe_forward_noalloc",
            "moe_pack_weights", "moe_set_path_thresholds", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
@@ -62,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_align.restype = ctypes.c_int
     lib.moe_forward.argtypes = [D, P, P, P, P, P, I32, P, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [D, P, P, P, P, P, I32, P, P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.moe_set_path_thresholds.argtypes = [I32, I32]
@@ -187,6 +190,21 @@ def moe_forward(desc, x, valid_rows, router_w, w13, w2, topk, out, workspace,
         _dev(w2, "w2", _w(desc), (E + ns, H, I)), topk,
         _dev(out, "out", _act(desc), (T, H)),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream)))
+
+
+def moe_forward_noalloc(desc, x, valid_rows, router_w, w13, w2, topk, out, stream=None):
+    """moe_forward in the library's fixed device scratch (no workspace)."""
+    T, H, E, I, ns = desc.T, desc.H, desc.E, desc.I, desc.n_shared
+    _check(load_library().moe_forward_noalloc(
+        ctypes.byref(desc), _dev(x, "x", _act(desc), (T, H)),
+        _dev(valid_rows, "valid_rows", torch.uint8, (T,)),
+        _dev(router_w, "router_w", _act(desc), (E, H)),
+        _dev(w13, "w13", _w(desc), (E + ns, 2 * I, H)),
+        _dev(w2, "w2", _w(desc), (E + ns, H, I)), topk,
+        _dev(out, "out", _act(desc), (T, H)), _stream(stream)))
+
+
+SCRATCH_BYTES = 64 << 20   # MOE_SCRATCH_BYTES
 
 
 def moe_pack_weights(desc, w13, w2, w13_packed=None, w2_packed=None, stream=None):

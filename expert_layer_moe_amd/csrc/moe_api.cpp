@@ -220,6 +220,118 @@ hipError_t launch_logits(const Plan& p, const void* x, const uint8_t* valid,
                                   p.ks, s);
 }
 
+// The launch sequence of one layer forward into a workspace of p.total bytes
+// (arguments already validated).
+int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                 const void* router_w, const void* w13, const void* w2, void* out,
+                 void* workspace, hipStream_t s) {
+  void* ws = workspace;
+  float* part = at<float>(ws, p.off_part);
+  int32_t* ids = at<int32_t>(ws, p.off_ids);
+  float* wts = at<float>(ws, p.off_w);
+  int32_t* sorted = at<int32_t>(ws, p.off_sorted);
+  int32_t* bexp = at<int32_t>(ws, p.off_bexp);
+  int32_t* offs = at<int32_t>(ws, p.off_offs);
+  int32_t* npost = at<int32_t>(ws, p.off_npost);
+  int32_t* slot = at<int32_t>(ws, p.off_slot);
+  int32_t* cnt = at<int32_t>(ws, p.off_cnt);
+  int32_t* tseg = at<int32_t>(ws, p.off_tseg);
+  int32_t* trow = at<int32_t>(ws, p.off_trow);
+  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
+  int32_t* iseg = at<int32_t>(ws, p.off_iseg);
+  int32_t* irow = at<int32_t>(ws, p.off_irow);
+  int32_t* nitems = at<int32_t>(ws, p.off_nitems);
+  const bool gemm = p.big_thr != INT_MAX;
+  void* h = at<void>(ws, p.off_h);
+  void* y = at<void>(ws, p.off_y);
+  const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
+  const bool packed = desc->w_layout == MOE_LAYOUT_FRAG16;
+
+  {
+    StageTimer tm(S_LOGITS, s);
+    if (launch_logits(p, x, valid_rows, router_w, part, s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_TOPK, s);
+    if (moe::launch_route_topk(part, p.ks, valid_rows, p.T, p.E, p.k, ids, wts,
+                               nullptr, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_ALIGN, s);
+    if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
+                          slot, cnt, p.big_thr, p.min_tiles, gemm ? tseg : nullptr, trow,
+                          ntiles, at<int32_t>(ws, p.off_span), iseg, irow, nitems,
+                          s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (wkind != moe::W_F32) {
+    StageTimer tm(S_PACK_X, s);
+    if (moe::launch_pack_x(x, sorted, bexp, npost, cnt, p.big_thr, gemm ? ntiles : nullptr, y,
+                           p.H, p.k, p.bm, p.cap, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_GATE_UP, s);
+    if (moe::launch_gate_up(wkind, packed, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
+                            cnt, iseg, irow, nitems, p.max_items, y, h, p.H, p.I, p.k, p.bm,
+                            p.cap, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (gemm) {
+    StageTimer tm(S_GATE_UP_GEMM, s);
+    if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, packed, x, w13, desc->w13_scale, sorted, tseg,
+                                 trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles,
+                                 s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_DOWN, s);
+    if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
+                         irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap,
+                         s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  if (gemm) {
+    StageTimer tm(S_DOWN_GEMM, s);
+    if (moe::launch_down_gemm(wkind == moe::W_FP8, packed, h, w2, desc->w2_scale, tseg, trow, ntiles,
+                              offs, cnt, y, p.H, p.I, p.max_tiles, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  {
+    StageTimer tm(S_COMBINE, s);
+    if (moe::launch_combine(y, p.w == MOE_FP8_E4M3, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+                            p.act == MOE_BF16, s) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+
+// ---- fixed device scratch of moe_forward_noalloc ------------------------------
+// One array per GPU, held from the library's load until the process ends.
+// Host code never uses its name as an address: the device address of each
+// GPU's copy comes from hipGetSymbolAddress, resolved once per device.
+constexpr size_t kScratchBytes = size_t(MOE_SCRATCH_BYTES);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This GPU's scratch (the current device), or nullptr on a HIP error.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 }  // namespace
 
 extern "C" {
@@ -323,87 +435,22 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   if (st != MOE_OK) return st;
   if (!x || !router_w || !w13 || !w2 || !out || !workspace) return MOE_ERR_INVALID_ARG;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  void* ws = workspace;
-  float* part = at<float>(ws, p.off_part);
-  int32_t* ids = at<int32_t>(ws, p.off_ids);
-  float* wts = at<float>(ws, p.off_w);
-  int32_t* sorted = at<int32_t>(ws, p.off_sorted);
-  int32_t* bexp = at<int32_t>(ws, p.off_bexp);
-  int32_t* offs = at<int32_t>(ws, p.off_offs);
-  int32_t* npost = at<int32_t>(ws, p.off_npost);
-  int32_t* slot = at<int32_t>(ws, p.off_slot);
-  int32_t* cnt = at<int32_t>(ws, p.off_cnt);
-  int32_t* tseg = at<int32_t>(ws, p.off_tseg);
-  int32_t* trow = at<int32_t>(ws, p.off_trow);
-  int32_t* ntiles = at<int32_t>(ws, p.off_ntiles);
-  int32_t* iseg = at<int32_t>(ws, p.off_iseg);
-  int32_t* irow = at<int32_t>(ws, p.off_irow);
-  int32_t* nitems = at<int32_t>(ws, p.off_nitems);
-  const bool gemm = p.big_thr != INT_MAX;
-  void* h = at<void>(ws, p.off_h);
-  void* y = at<void>(ws, p.off_y);
-  const int wkind = p.w == MOE_F32 ? moe::W_F32 : (p.w == MOE_BF16 ? moe::W_BF16 : moe::W_FP8);
-  const bool packed = desc->w_layout == MOE_LAYOUT_FRAG16;
+  return forward_impl(p, desc, x, valid_rows, router_w, w13, w2, out, workspace,
+                      static_cast<hipStream_t>(stream));
+}
 
-  {
-    StageTimer tm(S_LOGITS, s);
-    if (launch_logits(p, x, valid_rows, router_w, part, s) != hipSuccess) return MOE_ERR_HIP;
-  }
-  {
-    StageTimer tm(S_TOPK, s);
-    if (moe::launch_route_topk(part, p.ks, valid_rows, p.T, p.E, p.k, ids, wts,
-                               nullptr, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  {
-    StageTimer tm(S_ALIGN, s);
-    if (moe::launch_align(ids, p.T, p.k, p.E, p.ns, p.bm, sorted, bexp, offs, npost,
-                          slot, cnt, p.big_thr, p.min_tiles, gemm ? tseg : nullptr, trow,
-                          ntiles, at<int32_t>(ws, p.off_span), iseg, irow, nitems,
-                          s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  if (wkind != moe::W_F32) {
-    StageTimer tm(S_PACK_X, s);
-    if (moe::launch_pack_x(x, sorted, bexp, npost, cnt, p.big_thr, gemm ? ntiles : nullptr, y,
-                           p.H, p.k, p.bm, p.cap, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  {
-    StageTimer tm(S_GATE_UP, s);
-    if (moe::launch_gate_up(wkind, packed, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
-                            cnt, iseg, irow, nitems, p.max_items, y, h, p.H, p.I, p.k, p.bm,
-                            p.cap, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  if (gemm) {
-    StageTimer tm(S_GATE_UP_GEMM, s);
-    if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, packed, x, w13, desc->w13_scale, sorted, tseg,
-                                 trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles,
-                                 s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  {
-    StageTimer tm(S_DOWN, s);
-    if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
-                         irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap,
-                         s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  if (gemm) {
-    StageTimer tm(S_DOWN_GEMM, s);
-    if (moe::launch_down_gemm(wkind == moe::W_FP8, packed, h, w2, desc->w2_scale, tseg, trow, ntiles,
-                              offs, cnt, y, p.H, p.I, p.max_tiles, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  {
-    StageTimer tm(S_COMBINE, s);
-    if (moe::launch_combine(y, p.w == MOE_FP8_E4M3, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
-                            p.act == MOE_BF16, s) != hipSuccess)
-      return MOE_ERR_HIP;
-  }
-  return MOE_OK;
+int moe_forward_noalloc(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                        const void* router_w, const void* w13, const void* w2,
+                        int32_t topk, void* out, moe_stream_t stream) {
+  Plan p;
+  const int st = make_plan(desc, topk, &p);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !w13 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+  if (p.total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  return forward_impl(p, desc, x, valid_rows, router_w, w13, w2, out, ws,
+                      static_cast<hipStream_t>(stream));
 }
 
 int moe_num_stages(void) { return S_COUNT; }

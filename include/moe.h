@@ -161,6 +161,27 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
                 int32_t topk, void* out, void* workspace,
                 size_t workspace_bytes, moe_stream_t stream);
 
+/* Bytes of the fixed device scratch that moe_forward_noalloc works in. */
+#define MOE_SCRATCH_BYTES (64u << 20)
+
+/* moe_forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP-graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, kernels and output bits as
+ * moe_forward, minus the workspace: the layer runs in a static device array
+ * of MOE_SCRATCH_BYTES (64 MiB) that each GPU holds from the library's load
+ * until the process ends (enough for decode-sized batches: the 48-expert
+ * top-3 layer of hidden 7168 and inter 640 takes 44 MiB at 256 rows).
+ * Returns MOE_ERR_WORKSPACE, before any launch, when
+ * moe_workspace_size(desc, topk) exceeds it.  Nothing is allocated and no
+ * library routine that allocates is called; the first call on a GPU looks up
+ * that GPU's copy of the array.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (two streams, two threads)
+ * race and give undefined results: serialise them.  Nothing in the array
+ * needs to start at zero (each call writes what it reads). */
+int moe_forward_noalloc(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                        const void* router_w, const void* w13, const void* w2,
+                        int32_t topk, void* out, moe_stream_t stream);
+
 /* One-time re-layout of the expert weights (at load time) into the order in
  * which the layer's MFMA kernels fetch them, so that each wave-wide weight
  * load is one contiguous 1 KB (bf16) / 512 B (fp8) block instead of 16 rows x

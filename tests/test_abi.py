@@ -158,3 +158,25 @@ def test_profile_hooks_without_records():
                                  "gate_up_gemm", "down", "down_gemm", "combine"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())
+
+
+def test_noalloc_validation_before_any_launch():
+    """Bad descriptors, null pointers and layers whose workspace exceeds the
+    fixed scratch are rejected before the scratch is looked up."""
+    lib = moe.load_library()
+    F = lambda d, k=3, x=FAKE: lib.moe_forward_noalloc(
+        ctypes.byref(d) if d is not None else None, x, None, FAKE, FAKE, FAKE, k, FAKE, None)
+    assert F(None) == -1
+    assert F(_d(T=0)) == -1
+    assert F(_d(H=7200)) == -2
+    assert F(_d(), x=None) == -1
+    assert F(_d(), k=0) == -1
+    big = _d(T=8192)
+    assert lib.moe_workspace_size(ctypes.byref(big), 3) > moe.SCRATCH_BYTES
+    assert F(big) == -3
+
+
+def test_scratch_bytes_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define MOE_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.SCRATCH_BYTES
