@@ -162,10 +162,13 @@ __device__ void pad_segments(const int* cnt, const int* base, int nseg, int bm,
 
 // Stable scatter of the assignments [a0, a1), chunk by chunk in flat order;
 // base[seg] (LDS) is the next free position of each segment and advances.
-// wcnt must be zero on entry and is zero on exit.
+// on_pos(a, pos, entry) receives each valid assignment's position in the
+// sorted list and its entry (t * k + j; t * k for the shared slot).  A chunk
+// of padding rows only is skipped.  wcnt must be zero on entry and is zero
+// on exit.
+template <typename OnPos>
 __device__ void scatter_range(const int32_t* ids, int a0, int a1, int k, int kk, int E,
-                              int nseg, int* base, int (*wcnt)[kMaxSeg], int32_t* sorted_ids,
-                              int32_t* slot_pos) {
+                              int nseg, int* base, int (*wcnt)[kMaxSeg], OnPos on_pos) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   for (int chunk = a0; chunk < a1; chunk += kAlignThreads) {
@@ -181,14 +184,12 @@ __device__ void scatter_range(const int32_t* ids, int a0, int a1, int k, int kk,
     }
     const int rank = __popcll(same & lt_mask);
     if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(same);
-    __syncthreads();
+    if (!__syncthreads_or(e >= 0)) continue;
     if (e >= 0) {
       int pre = 0;
       for (int w = 0; w < wave; ++w) pre += wcnt[w][e];
-      const int pos = base[e] + pre + rank;
       const int t = a / kk, j = a - t * kk;
-      sorted_ids[pos] = t * k + (j < k ? j : 0);
-      if (slot_pos) slot_pos[a] = pos;
+      on_pos(a, base[e] + pre + rank, t * k + (j < k ? j : 0));
     }
     __syncthreads();
     for (int seg = tid; seg < nseg; seg += kAlignThreads) {
@@ -202,6 +203,16 @@ __device__ void scatter_range(const int32_t* ids, int a0, int a1, int k, int kk,
     __syncthreads();
   }
 }
+
+// on_pos of the align: the sorted list and each assignment's position in it
+struct StoreSorted {
+  int32_t* sorted_ids;
+  int32_t* slot_pos;
+  __device__ void operator()(int a, int pos, int entry) const {
+    sorted_ids[pos] = entry;
+    if (slot_pos) slot_pos[a] = pos;
+  }
+};
 
 // One 1024-thread block for the whole list (small batches).
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
@@ -233,7 +244,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   scan_segments(cnt, base, nseg, bm, offsets, n_post, big_thr, min_tiles, tile_seg, tile_row0,
                 n_tiles, item_seg, item_row0, n_items);
   pad_segments(cnt, base, nseg, bm, sorted_ids, block_expert, seg_count);
-  scatter_range(ids, 0, n_assign, k, kk, E, nseg, base, wcnt, sorted_ids, slot_pos);
+  scatter_range(ids, 0, n_assign, k, kk, E, nseg, base, wcnt, StoreSorted{sorted_ids, slot_pos});
 }
 
 // Large batches, three launches over kAlignSpan-assignment spans:
@@ -325,7 +336,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
     (&wcnt[0][0])[i] = 0;
   __syncthreads();
   const int a0 = blockIdx.x * kAlignSpan, a1 = min(n_assign, a0 + kAlignSpan);
-  scatter_range(ids, a0, a1, k, kk, E, nseg, base, wcnt, sorted_ids, slot_pos);
+  scatter_range(ids, a0, a1, k, kk, E, nseg, base, wcnt, StoreSorted{sorted_ids, slot_pos});
 }
 
 }  // namespace

@@ -460,23 +460,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 // Tile q's A row j is output column 32 (q / 2) + 8 (j / 4) + 4 (q % 2) + j % 4,
 // so lane (g, m) ends with columns 8 g .. 8 g + 7 and 32 + 8 g .. 32 + 8 g + 7
 // of its row.
-template <int KSTEPS, bool PW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void down_tall_f8s_kernel(
+// One block's tile in NH 64-row halves: 2, or 1 for a tile of at most 64
+// rows (typically an expert's last), which then issues half the MFMAs.
+template <int KSTEPS, bool PW, int NH>
+__device__ __forceinline__ void down_f8s_tile(
     const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
-    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
-    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
-    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ y, int H, int n_chunks,
-    int max_tiles) {
+    uint16_t* __restrict__ y, int H, int e, int ch, int row_base, int rows_here,
+    u32x4 (*hbuf)[kWave]) {
   constexpr int I = 32 * KSTEPS;
   constexpr int KB = I / 128;      // scale blocks along K
-  __shared__ u32x4 hbuf[8 * KSTEPS][kWave];
-  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
-  if (lid < 0) return;
-  const int mt_id = lid / n_chunks, ch = lid - mt_id * n_chunks;
-  const int e = tile_seg[mt_id];
-  const int r0 = tile_row0[mt_id];
-  const int row_base = seg_off[e] + r0;
-  const int rows_here = min(kBM, seg_cnt[e] - r0);
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int m = lane % 16, g = lane / 16;
@@ -508,7 +500,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       for (int q = 0; q < 4; ++q) wq[st][q] = w_code(tile_n0(0), st, q);
   }
 #pragma unroll
-  for (int i = 0; i < 128 * I / 8 / 256; ++i) {
+  for (int i = 0; i < 64 * NH * I / 8 / 256; ++i) {
     const int P = i * 256 + tid;
     const int row = P / (I / 8), kp = P - row * (I / 8);
     const int rr = min(row, rows_here - 1);
@@ -537,7 +529,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     load_scales(n1);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < NH; ++half) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -547,7 +539,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         bf16x8 wa[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) wa[q] = fp8x8_to_bf16x8(wq[st][q][0], wq[st][q][1]);
-        if (half == 1) {
+        if (half == NH - 1) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) wq[st][q] = w_code(n1, st, q);
         }
@@ -574,6 +566,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
     }
   }
+}
+
+template <int KSTEPS, bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void down_tall_f8s_kernel(
+    const uint16_t* __restrict__ h, const uint8_t* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ y, int H, int n_chunks,
+    int max_tiles) {
+  __shared__ u32x4 hbuf[8 * KSTEPS][kWave];
+  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
+  if (lid < 0) return;
+  const int mt_id = lid / n_chunks, ch = lid - mt_id * n_chunks;
+  const int e = tile_seg[mt_id];
+  const int r0 = tile_row0[mt_id];
+  const int row_base = seg_off[e] + r0;
+  const int rows_here = min(kBM, seg_cnt[e] - r0);
+  if (rows_here <= kBM / 2)
+    down_f8s_tile<KSTEPS, PW, 1>(h, w2, s2, y, H, e, ch, row_base, rows_here, hbuf);
+  else
+    down_f8s_tile<KSTEPS, PW, 2>(h, w2, s2, y, H, e, ch, row_base, rows_here, hbuf);
 }
 
 // Gate/up of the large segments: 128 sorted rows x (128 gate + the matching
