@@ -394,6 +394,8 @@ def run_headline(args, name):
     }
     if args.gemm_min_rows is not None:
         res["config"]["gemm_thresholds"] = [args.gemm_min_rows, args.gemm_min_tiles]
+    if wl.cfg.w == "fp8":
+        res["config"]["fp8_gate_up_gemm"] = "fp8_mfma_two_term" if args.fp8_mfma else "bf16_mfma"
     if dom:
         g_ms, g_n = dom_rec[dom]
         roof = roofline(wl, dom, g_ms / max(g_n, 1) / 1e3)
@@ -433,6 +435,8 @@ def run(args):
     moe.load_library()
     if args.gemm_min_rows is not None:
         moe.moe_set_path_thresholds(args.gemm_min_rows, args.gemm_min_tiles)
+    if args.fp8_mfma:
+        moe.moe_set_fp8_mfma(True)
     if args.copy_calibrate:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -470,6 +474,9 @@ def main():
                     help="... once their 128-row tiles number this many (-1: fill the chip)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay pass")
+    ap.add_argument("--fp8-mfma", action="store_true",
+                    help="fp8 weights on the tiled gate/up GEMM: fp8 MFMA on two-term token "
+                         "codes instead of bf16 MFMA on dequantised weights")
     ap.add_argument("--row-major", action="store_true",
                     help="time the expert weights in the row-major layout they are handed over in")
     args = ap.parse_args()

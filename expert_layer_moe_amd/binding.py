@@ -23,7 +23,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
            "moe_forward_noalloc",
-           "moe_pack_weights", "moe_set_path_thresholds", "moe_status_str", "moe_num_stages", "moe_stage_name",
+           "moe_pack_weights", "moe_set_path_thresholds", "moe_set_fp8_mfma", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
 
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
     lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_set_fp8_mfma.argtypes = [I32]
+    lib.moe_set_fp8_mfma.restype = ctypes.c_int
     lib.moe_set_path_thresholds.argtypes = [I32, I32]
     lib.moe_set_path_thresholds.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -226,6 +228,13 @@ def moe_set_path_thresholds(gemm_min_rows: int = 128, gemm_min_tiles: int = -1):
     """Segments above gemm_min_rows rows use the tiled GEMM kernels once their
     tiles number gemm_min_tiles (-1 = fill the chip).  Process-wide."""
     _check(load_library().moe_set_path_thresholds(gemm_min_rows, gemm_min_tiles))
+
+
+def moe_set_fp8_mfma(enable: bool = False):
+    """fp8 weights on the tiled gate/up GEMM: fp8 MFMA on two-term token
+    codes (True) or bf16 MFMA on dequantised weights (False, the default).
+    Process-wide; size workspaces after choosing."""
+    _check(load_library().moe_set_fp8_mfma(1 if enable else 0))
 
 
 def moe_status_str(status: int) -> str:

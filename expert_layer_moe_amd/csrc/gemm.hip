@@ -758,6 +758,217 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void g
   }
 }
 
+// Gate/up of the large segments with fp8 weights on the fp8 MFMA (32x32x64,
+// e4m3 x e4m3, fp32 accumulation).  The token rows come as two e4m3 terms
+// that share one power-of-two row scale, x = s_t (hi + lo) (xq_split_kernel),
+// so each 64-wide K step of W13 codes meets both terms and both MFMAs
+// accumulate into one sum: the same MFMA cycles as the bf16 instruction on
+// dequantised weights, with the weights' codes used as they are.  Block,
+// wave and epilogue layout as gate_up_tall_kernel: 128 sorted rows x (128
+// gate + the matching 128 up columns); each wave's 32 + 32 weight rows are
+// the A operands straight from memory (a lane holds 32 codes of one row:
+// K 32 hh .. 32 hh + 31 of the step, hh = lane / 32), the x codes of each
+// 64-wide K window come through two LDS buffers (rows 80 bytes apart: the
+// 16-byte operand reads of 8 consecutive lanes hit distinct banks) as the B
+// operands (token 32 n + lane % 32, the same K bytes).
+// Block scales of the weights (one per 128 rows x 128 K): the accumulator
+// holds the sum in units of a current scale c, multiplied by c_old / c_new
+// when a 128-wide K block begins; a scale smaller in magnitude than 2^-64 of
+// the row block's largest (zero included) is raised to that bound, which
+// keeps every ratio below 2^64 and the accumulator finite.  At the end the
+// sum is multiplied by c and by the row scale s_t.
+constexpr int kF8KW = 64;            // K window: one fp8 MFMA K step
+constexpr int kF8RS = kF8KW + 16;    // LDS row stride of the x codes, bytes
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+template <bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void gate_up_f8x_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ sx, const uint8_t* __restrict__ w13,
+    const float* __restrict__ s13, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
+    const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ h, int T, int H, int I, int k,
+    int n_nt, int max_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[2][2][kBM][kF8RS];  // [buf][term][row][K]
+  __shared__ float wsc[2][kMaxScaleCols];   // gate / up scale rows of weight row block nt
+  __shared__ float wfloor[2];
+  __shared__ float tsc[kBM];                // row scales of the tile's tokens
+  const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_nt);
+  if (lid < 0) return;
+  const int mt_id = lid / n_nt, nt = lid - mt_id * n_nt;
+  const int e = tile_seg[mt_id];
+  const int r0 = tile_row0[mt_id];
+  const int row_base = seg_off[e] + r0;
+  const int rows_here = min(kBM, seg_cnt[e] - r0);
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int l32 = lane % 32, hh = lane / 32;
+
+  // x staging: per window 2 terms x 128 rows x 64 B = 16 KB; a thread moves
+  // 16-byte piece tid % 4 of rows tid / 4 and tid / 4 + 64, both terms
+  const int xp = tid & 3;
+  uint32_t xoff[2];
+  int xrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xrow[i] = (tid >> 2) + 64 * i;
+    const int rr = min(xrow[i], rows_here - 1);
+    xoff[i] = (uint32_t)((size_t)(sorted_ids[row_base + rr] / k) * H) + 16 * xp;
+  }
+  const uint8_t* xlo = xq + (size_t)T * H;
+  if (tid < kBM) tsc[tid] = sx[sorted_ids[row_base + min(tid, rows_here - 1)] / k];
+  const int nkb = H / 128;
+  {
+    const float* sb = s13 + (size_t)e * (2 * I / 128) * nkb;
+    for (int i = tid; i < 2 * nkb; i += 256)
+      wsc[i / nkb][i % nkb] = sb[(size_t)(i < nkb ? nt : I / 128 + nt) * nkb + i % nkb];
+  }
+
+  // A operands: gate (q = 0) / up (q = 1) row of this lane, 32 codes at
+  // K 64 w + 32 hh of window w
+  const size_t wexp = (size_t)e * 2 * I * H;
+  size_t woff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = q * I + nt * 128 + wave * 32 + l32;
+    if constexpr (PW) woff[q] = wexp + ((size_t)(row / 16) * (H / 32) + hh) * 512 + 8 * (row % 16);
+    else woff[q] = wexp + (size_t)row * H + 32 * hh;
+  }
+  struct WStage { u32x4 c[2][2]; };   // [q][16-byte half]
+  struct XStage { u32x4 a[2][2]; };   // [row i][term]
+  auto w_load = [&](WStage& W, int win) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (PW) {
+        // fragment order: the 32 codes are four 8-byte pieces, 128 bytes apart
+        const uint8_t* p = w13 + woff[q] + (size_t)win * 1024;
+        const u32x2 a = ld8(p), b = ld8(p + 128), c = ld8(p + 256), d = ld8(p + 384);
+        W.c[q][0] = u32x4{a[0], a[1], b[0], b[1]};
+        W.c[q][1] = u32x4{c[0], c[1], d[0], d[1]};
+      } else {
+        const uint8_t* p = w13 + woff[q] + (size_t)win * kF8KW;
+        W.c[q][0] = ld16(p);
+        W.c[q][1] = ld16(p + 16);
+      }
+    }
+  };
+  auto x_load = [&](XStage& S, int win) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      S.a[i][0] = ld16(xq + xoff[i] + (uint32_t)win * kF8KW);
+      S.a[i][1] = ld16(xlo + xoff[i] + (uint32_t)win * kF8KW);
+    }
+  };
+  auto x_store = [&](const XStage& S, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        *reinterpret_cast<u32x4*>(&xbuf[buf][t][xrow[i]][16 * xp]) = S.a[i][t];
+  };
+
+  floatx16 acc[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][n][r] = 0.f;
+  float cur[2] = {1.f, 1.f};   // the accumulators' current scale unit
+  auto compute = [&](const WStage& W, int buf, int win) {
+    if ((win & 1) == 0) {
+      // a 128-wide K block begins: move the sums to its scale
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float sc = wsc[q][win >> 1];
+        const float se = fabsf(sc) < wfloor[q] ? (sc < 0.f ? -wfloor[q] : wfloor[q]) : sc;
+        const float ratio = cur[q] / se;
+        cur[q] = se;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[q][n][r] *= ratio;
+      }
+    }
+    i32x8 a[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a[q] = i32x8{(int)W.c[q][0][0], (int)W.c[q][0][1], (int)W.c[q][0][2], (int)W.c[q][0][3],
+                   (int)W.c[q][1][0], (int)W.c[q][1][1], (int)W.c[q][1][2], (int)W.c[q][1][3]};
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint8_t* xr = &xbuf[buf][t][32 * n + l32][32 * hh];
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(xr);
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(xr + 16);
+        const i32x8 b = i32x8{(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                              (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          acc[q][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[q], b, acc[q][n], 0, 0, 0,
+                                                                     0, 0, 0);
+      }
+  };
+
+  // windows in pairs (H / 64 is even): stage names fixed, loads two windows
+  // ahead (past the end they re-read the last window, unused)
+  const int nwin = H / kF8KW, last = nwin - 1;
+  XStage xs0, xs1;
+  WStage ws0, ws1;
+  x_load(xs0, 0);
+  w_load(ws0, 0);
+  x_load(xs1, min(1, last));
+  w_load(ws1, min(1, last));
+  __syncthreads();   // scale rows and token scales in LDS
+  if (wave < 2) {
+    // bound below which a block scale is raised: 2^-64 of the row block's
+    // largest magnitude (the smallest normal float if all are zero)
+    float m = 0.f;
+    for (int i = lane; i < nkb; i += kWave) m = fmaxf(m, fabsf(wsc[wave][i]));
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) wfloor[wave] = fmaxf(m * 0x1p-64f, 0x1p-126f);
+  }
+  x_store(xs0, 0);
+  __syncthreads();
+  x_load(xs0, min(2, last));
+  for (int win = 0; win < nwin; win += 2) {
+    compute(ws0, 0, win);
+    w_load(ws0, min(win + 2, last));
+    x_store(xs1, 1);
+    __syncthreads();
+    x_load(xs1, min(win + 3, last));
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ws1, 1, win + 1);
+    w_load(ws1, min(win + 3, last));
+    x_store(xs0, 0);
+    __syncthreads();
+    x_load(xs0, min(win + 4, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // acc[q][n] lane (l32, hh) register r: column 32 wave + 8 (r / 4) + 4 hh +
+  // r % 4 of the block's 128 (gate q = 0, up q = 1), sorted row 32 n + l32
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int row = 32 * n + l32;
+    if (row >= rows_here) continue;
+    const float fg = cur[0] * tsc[row], fu = cur[1] * tsc[row];
+    uint16_t* hr = h + (size_t)(row_base + row) * I + nt * 128 + wave * 32 + 4 * hh;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(silu_mul(acc[0][n][4 * c] * fg, acc[1][n][4 * c] * fu),
+                          silu_mul(acc[0][n][4 * c + 1] * fg, acc[1][n][4 * c + 1] * fu));
+      pk[1] = pack_bf16x2(silu_mul(acc[0][n][4 * c + 2] * fg, acc[1][n][4 * c + 2] * fu),
+                          silu_mul(acc[0][n][4 * c + 3] * fg, acc[1][n][4 * c + 3] * fu));
+      *reinterpret_cast<u32x2*>(hr + 8 * c) = pk;
+    }
+  }
+}
+
 // Router logits of large batches with gate_up_tall_kernel's structure:
 // 128 consecutive token rows x 256 experts per block over one K chunk z of
 // ks.  Each wave owns 64 experts: two 32-row A operands of R (row-major,
@@ -941,10 +1152,25 @@ hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void*
                                const int32_t* tile_seg, const int32_t* tile_row0,
                                const int32_t* n_tiles, const int32_t* seg_off,
                                const int32_t* seg_cnt, void* h, int H, int I, int k,
-                               int max_tiles, hipStream_t s) {
+                               int max_tiles, const uint8_t* xq, const float* sx, int T,
+                               hipStream_t s) {
   if (H % 128 != 0 || I % 128 != 0 || H > kMaxGemmK) return hipErrorInvalidValue;
   const int n_nt = I / 128;
   const dim3 grid(round8g(max_tiles * n_nt));
+  if (fp8 && xq != nullptr) {
+    // fp8 MFMA on the two-term token codes
+    const uint8_t* wq = static_cast<const uint8_t*>(w13);
+    uint16_t* hb = static_cast<uint16_t*>(h);
+    if (packed)
+      hipLaunchKernelGGL((gate_up_f8x_kernel<true>), grid, dim3(256), 0, s, xq, sx, wq, s13,
+                         sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, hb, T, H, I,
+                         k, n_nt, max_tiles);
+    else
+      hipLaunchKernelGGL((gate_up_f8x_kernel<false>), grid, dim3(256), 0, s, xq, sx, wq, s13,
+                         sorted_ids, tile_seg, tile_row0, n_tiles, seg_off, seg_cnt, hb, T, H, I,
+                         k, n_nt, max_tiles);
+    return hipGetLastError();
+  }
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* hb = static_cast<uint16_t*>(h);
 #define MOE_GUT(F8, P)                                                                      \

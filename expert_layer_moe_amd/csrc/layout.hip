@@ -48,6 +48,64 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
     *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = ld16(src + 32 * s);
 }
 
+// Token rows as two e4m3 terms for the fp8-MFMA gate/up GEMM: with one
+// power-of-two scale per row, s = 2^(e - 8) where max_h |x[t,h]| = m 2^e
+// (m in [0.5, 1); s = 1 for a zero row), every |x / s| is below 256;
+// hi = e4m3(x / s) and lo = e4m3(x / s - hi), both rounded to nearest even,
+// so x = s (hi + lo) up to the part of x / s - hi below e4m3's resolution
+// (a bf16 value carries 8 significant bits, hi and lo 4 each).  Planes
+// xq[0..T*H) (hi) and xq[T*H..2*T*H) (lo), row-major; sx[t] = s.  Padding
+// rows are neither read nor written.  One wave per row, two passes over it
+// (the second from cache).
+__global__ __launch_bounds__(256) void xq_split_kernel(const uint16_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ valid,
+                                                       uint8_t* __restrict__ xq,
+                                                       float* __restrict__ sx, int T, int H) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T || (valid != nullptr && valid[t] == 0)) return;
+  const uint16_t* row = x + (size_t)t * H;
+  float amax = 0.f;
+  for (int p = lane; p < H / 8; p += kWave) {
+    const u32x4 v = ld16(row + 8 * p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[q] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(v[q] & 0xffff0000u)));
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  int e = 0;
+  (void)frexpf(amax, &e);
+  const bool zero = !(amax > 0.f);
+  const float inv = zero ? 1.f : ldexpf(1.f, 8 - e);   // 1 / s, exact
+  if (lane == 0) sx[t] = zero ? 1.f : ldexpf(1.f, e - 8);
+  uint8_t* hi = xq + (size_t)t * H;
+  uint8_t* lo = hi + (size_t)T * H;
+  for (int p = lane; p < H / 8; p += kWave) {
+    const u32x4 v = ld16(row + 8 * p);
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f[2 * q] = __uint_as_float(v[q] << 16) * inv;
+      f[2 * q + 1] = __uint_as_float(v[q] & 0xffff0000u) * inv;
+    }
+    int ch[2], cl[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      int c = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w], f[4 * w + 1], 0, false);
+      ch[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w + 2], f[4 * w + 3], c, true);
+      const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(ch[w], false);
+      const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(ch[w], true);
+      c = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w] - h01[0], f[4 * w + 1] - h01[1], 0, false);
+      cl[w] = __builtin_amdgcn_cvt_pk_fp8_f32(f[4 * w + 2] - h23[0], f[4 * w + 3] - h23[1], c, true);
+    }
+    *reinterpret_cast<u32x2*>(hi + 8 * p) = u32x2{(uint32_t)ch[0], (uint32_t)ch[1]};
+    *reinterpret_cast<u32x2*>(lo + 8 * p) = u32x2{(uint32_t)cl[0], (uint32_t)cl[1]};
+  }
+}
+
 // Weights in MFMA B-fragment order (the same tile / step / lane order as
 // frag_index, over a [rows, K] matrix): block (16-row tile t, K step s) of
 // 512 elements at (t * K/32 + s) * 512, lane 16 g + m holding row 16 t + m,
@@ -194,6 +252,14 @@ hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t
                      s, static_cast<const uint16_t*>(x), sorted_ids, block_expert, n_post,
                      seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc,
                      bm / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_xq_split(const void* x, const uint8_t* valid, uint8_t* xq, float* sx, int T,
+                           int H, hipStream_t s) {
+  if (H % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(xq_split_kernel, dim3((T + 3) / 4), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), valid, xq, sx, T, H);
   return hipGetLastError();
 }
 

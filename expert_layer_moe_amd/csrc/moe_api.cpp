@@ -31,7 +31,8 @@ struct Plan {
   int max_items;  // bound on the streaming kernels' work items
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
       off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_iseg, off_irow, off_nitems,
-      off_span, off_h, off_y, total;
+      off_span, off_h, off_y, off_xq, off_sx, total;
+  bool xsplit;    // fp8 weights on the GEMM path: token rows as two e4m3 terms
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -42,6 +43,10 @@ constexpr int kBigSegRows = 128;
 // Path thresholds (moe_set_path_thresholds); read when a call is planned.
 std::atomic<int> g_gemm_min_rows{kBigSegRows};
 std::atomic<int> g_gemm_min_tiles{-1};   // -1: enough tiles to fill the chip
+// fp8 weights on the tiled gate/up GEMM: fp8 MFMA on two-term token codes (1)
+// or bf16 MFMA on dequantised weights (0, the default: the same MFMA cycles,
+// measured no faster, and no split pass); moe_set_fp8_mfma
+std::atomic<int> g_fp8_mfma{0};
 
 // Padding granularity of the expert segments in the sorted row list: every
 // kernel works on 16-row MFMA tiles of a segment (the tiled GEMMs on 128-row
@@ -121,10 +126,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->ks = choose_ks(d);
   p->router_gemm = use_router_gemm(d);
   const int min_rows = g_gemm_min_rows.load();
-  p->big_thr = (d->act_dtype == MOE_BF16 && d->I % 128 == 0 && d->H <= moe::kMaxGemmK &&
-                d->I <= moe::kMaxGemmK && fits_tiled(d))
-                   ? min_rows
-                   : INT_MAX;
+  const bool gemm_shape = d->act_dtype == MOE_BF16 && d->I % 128 == 0 &&
+                          d->H <= moe::kMaxGemmK && d->I <= moe::kMaxGemmK && fits_tiled(d);
+  p->big_thr = gemm_shape ? min_rows : INT_MAX;
   const size_t kk = (size_t)topk + p->ns;
   // the GEMM path only pays once its gate/up launch fills the chip
   // (256 blocks of I/128 columns each)
@@ -166,6 +170,13 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   // y rows (fp32; bf16 with fp8 weights) also hold the packed token rows of
   // the streaming gate/up (cap x H bf16) until the down kernels overwrite them
   p->off_y = take((size_t)p->cap * p->H * (p->w == MOE_FP8_E4M3 ? 2 : 4));
+  // two e4m3 code planes of the token rows and their scales (fp8 MFMA path):
+  // room whenever the shape can take the tiled GEMM (so the workspace size
+  // does not depend on the path thresholds); filled when it can run
+  const bool xq_room = p->w == MOE_FP8_E4M3 && gemm_shape && g_fp8_mfma.load() != 0;
+  p->xsplit = xq_room && p->big_thr != INT_MAX;
+  p->off_xq = take(xq_room ? (size_t)2 * p->T * p->H : 0);
+  p->off_sx = take(xq_room ? (size_t)p->T * 4 : 0);
   p->total = o;
   return MOE_OK;
 }
@@ -178,10 +189,10 @@ T* at(void* ws, size_t off) {
 // ---- measurement hooks -------------------------------------------------------
 enum Stage {
   S_LOGITS = 0, S_TOPK, S_ALIGN, S_PACK_X, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM,
-  S_COMBINE, S_COUNT
+  S_COMBINE, S_X_SPLIT, S_COUNT
 };
 const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "pack_x", "gate_up",
-                                    "gate_up_gemm", "down", "down_gemm", "combine"};
+                                    "gate_up_gemm", "down", "down_gemm", "combine", "x_split"};
 
 struct ProfRecord {
   int stage;
@@ -278,11 +289,17 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                             p.cap, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
+  uint8_t* xq = p.xsplit ? at<uint8_t>(ws, p.off_xq) : nullptr;
+  float* sx = p.xsplit ? at<float>(ws, p.off_sx) : nullptr;
+  if (p.xsplit) {
+    StageTimer tm(S_X_SPLIT, s);
+    if (moe::launch_xq_split(x, valid_rows, xq, sx, p.T, p.H, s) != hipSuccess) return MOE_ERR_HIP;
+  }
   if (gemm) {
     StageTimer tm(S_GATE_UP_GEMM, s);
     if (moe::launch_gate_up_gemm(wkind == moe::W_FP8, packed, x, w13, desc->w13_scale, sorted, tseg,
-                                 trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles,
-                                 s) != hipSuccess)
+                                 trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles, xq, sx,
+                                 p.T, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   {
@@ -363,6 +380,12 @@ int moe_set_path_thresholds(int32_t gemm_min_rows, int32_t gemm_min_tiles) {
   if (gemm_min_rows < 0 || gemm_min_tiles < -1) return MOE_ERR_INVALID_ARG;
   g_gemm_min_rows.store(gemm_min_rows);
   g_gemm_min_tiles.store(gemm_min_tiles);
+  return MOE_OK;
+}
+
+int moe_set_fp8_mfma(int32_t enable) {
+  if (enable != 0 && enable != 1) return MOE_ERR_INVALID_ARG;
+  g_fp8_mfma.store(enable);
   return MOE_OK;
 }
 

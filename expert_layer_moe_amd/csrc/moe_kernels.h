@@ -81,12 +81,19 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
                           int H, int I, int k, int bm, int max_rows, hipStream_t s);
 // Tiled GEMMs for segments with more than big_thr rows (the align's tile
 // table), and the router GEMM for large batches.  K (H, I) % 128 == 0.
+// fp8 weights with xq non-null: the fp8-MFMA kernel on the two-term token
+// codes (launch_xq_split); otherwise bf16 MFMA on dequantised weights.
 hipError_t launch_gate_up_gemm(bool fp8, bool packed, const void* x, const void* w13,
                                const float* s13, const int32_t* sorted_ids,
                                const int32_t* tile_seg, const int32_t* tile_row0,
                                const int32_t* n_tiles, const int32_t* seg_off,
                                const int32_t* seg_cnt, void* h, int H, int I, int k,
-                               int max_tiles, hipStream_t s);
+                               int max_tiles, const uint8_t* xq, const float* sx, int T,
+                               hipStream_t s);
+// Valid token rows (bf16 [T, H]) as two e4m3 terms with one power-of-two
+// scale per row: xq [2][T][H] (hi plane, lo plane), sx [T].
+hipError_t launch_xq_split(const void* x, const uint8_t* valid, uint8_t* xq, float* sx, int T,
+                           int H, hipStream_t s);
 hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2, const float* s2,
                             const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,

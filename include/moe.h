@@ -211,6 +211,20 @@ int moe_pack_weights(const moe_desc* desc, const void* w13, const void* w2,
  * gemm_min_rows < 0 or gemm_min_tiles < -1. */
 int moe_set_path_thresholds(int32_t gemm_min_rows, int32_t gemm_min_tiles);
 
+/* Arithmetic of the tiled gate/up GEMM for fp8 weights (host; process-wide,
+ * read when a call starts).  0 (default): bf16 MFMA on weights dequantised
+ * to bf16 (q * s rounded); 1: the fp8 MFMA on the weights' codes as they
+ * are, with each token row split into two e4m3 terms that share a
+ * power-of-two row scale (x = s (hi + lo), exact for all but the smallest
+ * elements of a row), two fp8 MFMAs where 0 issues four bf16 ones of the
+ * same total cycles.  Both meet the fp8-weight error bound; 1 needs 2 T H +
+ * 4 T bytes more workspace (moe_workspace_size follows the setting, so size
+ * workspaces after choosing) and a pass that splits the token rows
+ * ("Step3 Inference Optimization on AMD Instinct MI308X", optimisation list:
+ * mixed BF16 / FP8-blockscale arithmetic).  Returns MOE_ERR_INVALID_ARG for
+ * other values. */
+int moe_set_fp8_mfma(int32_t enable);
+
 /* Message for a status code (host; static string). */
 const char* moe_status_str(int status);
 

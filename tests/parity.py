@@ -50,6 +50,20 @@ def gemm_path(min_rows=16, min_tiles=1):
         moe.moe_set_path_thresholds()
 
 
+@contextlib.contextmanager
+def fp8_mfma(enable):
+    """fp8 weights on the tiled gate/up GEMM: fp8 MFMA on two-term token
+    codes (True) or bf16 MFMA on dequantised weights (False), for the
+    duration; restores the default.  Layers made inside size their
+    workspaces for the setting."""
+    import expert_layer_moe_amd as moe
+    moe.moe_set_fp8_mfma(enable)
+    try:
+        yield
+    finally:
+        moe.moe_set_fp8_mfma(False)
+
+
 def run_gpu(inp, layer=None, x=None, valid=None):
     layer = layer or device_layer(inp)
     xd = (inp.x if x is None else x).cuda()

@@ -155,7 +155,7 @@ def test_workspace_grows_with_batch():
 
 def test_profile_hooks_without_records():
     assert moe.stage_names() == ["route_logits", "route_topk", "align", "pack_x", "gate_up",
-                                 "gate_up_gemm", "down", "down_gemm", "combine"]
+                                 "gate_up_gemm", "down", "down_gemm", "combine", "x_split"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())
 
@@ -180,3 +180,28 @@ def test_scratch_bytes_matches_header():
     src = open(HEADER).read()
     m = re.search(r"#define MOE_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == moe.SCRATCH_BYTES
+
+
+def test_fp8_mfma_switch_and_workspace():
+    """The fp8 gate/up GEMM's arithmetic is process-wide; the two-term token
+    codes (2 T H + 4 T bytes) are in the workspace only when that path can
+    run (fp8 weights, a batch large enough for the tiled GEMM)."""
+    lib = moe.load_library()
+    assert lib.moe_set_fp8_mfma(2) == -1 and lib.moe_set_fp8_mfma(-1) == -1
+    d = _d(T=8192, E=256, I=256, w_dtype=moe.MOE_FP8_E4M3, w13_scale=FAKE, w2_scale=FAKE)
+    try:
+        assert lib.moe_set_fp8_mfma(0) == 0
+        off = lib.moe_workspace_size(ctypes.byref(d), 8)
+        assert lib.moe_set_fp8_mfma(1) == 0
+        on = lib.moe_workspace_size(ctypes.byref(d), 8)
+        assert on - off >= 2 * 8192 * 7168 + 4 * 8192
+        # the size does not depend on the path thresholds
+        assert lib.moe_set_path_thresholds(16, 1) == 0
+        assert lib.moe_workspace_size(ctypes.byref(d), 8) == on
+        bf16 = _d(T=8192, E=256, I=256)
+        b = lib.moe_workspace_size(ctypes.byref(bf16), 8)
+        assert lib.moe_set_fp8_mfma(0) == 0
+        assert lib.moe_workspace_size(ctypes.byref(bf16), 8) == b   # bf16 weights: no codes
+    finally:
+        lib.moe_set_fp8_mfma(0)
+        lib.moe_set_path_thresholds(128, -1)

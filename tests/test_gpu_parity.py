@@ -10,7 +10,7 @@ import oracle
 from workloads import get_config, make_inputs
 from workloads.gen import random_small
 
-from .parity import TOL, compare, device_layer, gemm_path, log, run_gpu
+from .parity import TOL, compare, device_layer, fp8_mfma, gemm_path, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -215,25 +215,30 @@ def _gemm_capable(kw):
     return kw.get("act", "bf16") == "bf16" and kw["I"] % 128 == 0 and kw["H"] % 128 == 0
 
 
-@pytest.mark.parametrize("path", ["auto", "gemm"])
+@pytest.mark.parametrize("path", ["auto", "gemm", "gemm-fp8mfma"])
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("i", range(len(SMALL)))
 def test_small_layers_match_oracle(i, packed, path):
     """path "gemm": segments above 16 rows take the tiled GEMM kernels (the
-    others stream), so both expert paths meet in one call."""
+    others stream), so both expert paths meet in one call; "gemm-fp8mfma":
+    the same with the fp8 MFMA on two-term token codes instead of fp8
+    weights dequantised for bf16 MFMA."""
     kw = SMALL[i]
     if packed and kw.get("w") == "f32":
         pytest.skip("fp32 weights have no packed layout")
-    if path == "gemm" and not _gemm_capable(kw):
+    if path != "auto" and not _gemm_capable(kw):
         pytest.skip("shape outside the tiled GEMM kernels")
+    if path == "gemm-fp8mfma" and kw.get("w") != "fp8":
+        pytest.skip("the fp8 MFMA setting only concerns fp8 weights")
     log(f"[case] small layer {i} packed={packed} path={path}: {kw}")
     inp = random_small(seed=100 + i, **kw)
-    layer = device_layer(inp, packed=packed)
-    if path == "gemm":
-        with gemm_path():
+    with fp8_mfma(path == "gemm-fp8mfma"):
+        layer = device_layer(inp, packed=packed)
+        if path == "auto":
             gpu = run_gpu(inp, layer)
-    else:
-        gpu = run_gpu(inp, layer)
+        else:
+            with gemm_path():
+                gpu = run_gpu(inp, layer)
     compare(inp, gpu)
 
 
@@ -281,7 +286,7 @@ def test_packed_weights_give_identical_output(kw, path):
     assert np.array_equal(a["out"], b["out"])
 
 
-@pytest.mark.parametrize("path", ["auto", "gemm"])
+@pytest.mark.parametrize("path", ["auto", "gemm", "gemm-fp8mfma"])
 @pytest.mark.parametrize("packed", [False, True])
 def test_fp8_zero_and_tiny_block_scales(packed, path):
     """W2 blocks whose first or second 128-wide K block has a zero scale, or a
@@ -301,11 +306,16 @@ def test_fp8_zero_and_tiny_block_scales(packed, path):
                 s2[e, nb, 1] = s2[e, nb, 0] * 1e-25
     inp.s2 = s2
     s13 = inp.s13.clone()
-    s13[0, :, 1] = 0.0
+    s13[0, :, 1] = 0.0                       # a zero K block in every gate/up row block
+    s13[1, 0, :] = 0.0                       # a gate row block with all scales zero
+    s13[2, :, 2] = s13[2, :, 0] * 1e-25      # a K block far below the others
+    s13[3, 1, 0] = -s13[3, 1, 0]             # a negative scale
     inp.s13 = s13
     log(f"[case] fp8 zero/tiny scales packed={packed} path={path}")
-    with gemm_path() if path == "gemm" else contextlib.nullcontext():
-        gpu = run_gpu(inp, device_layer(inp, packed=packed))
+    with fp8_mfma(path == "gemm-fp8mfma"):
+        layer = device_layer(inp, packed=packed)
+        with gemm_path() if path != "auto" else contextlib.nullcontext():
+            gpu = run_gpu(inp, layer)
     compare(inp, gpu)
 
 
@@ -328,6 +338,11 @@ def test_largest_gemm_k(w):
     compare(inp, run_gpu(inp, layer), ref=ref, tol=tol)
     with gemm_path():
         compare(inp, run_gpu(inp, layer), ref=ref, tol=tol)
+    if w == "fp8":
+        with fp8_mfma(True):
+            layer = device_layer(inp, packed=True)
+            with gemm_path():
+                compare(inp, run_gpu(inp, layer), ref=ref, tol=tol)
 
 
 @pytest.mark.parametrize("kw,path", [
