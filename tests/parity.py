@@ -64,6 +64,20 @@ def fp8_mfma(enable):
         moe.moe_set_fp8_mfma(False)
 
 
+@contextlib.contextmanager
+def one_stage(enable):
+    """Decode-sized batches: gate/up and down in one launch (True) or two, for
+    the duration; restores the default.  Layers made inside size their
+    workspaces for the setting.  (The path is switched off and the library
+    does not export the switch: only skipped tests use this.)"""
+    import expert_layer_moe_amd as moe
+    moe.moe_set_one_stage(enable)
+    try:
+        yield
+    finally:
+        moe.moe_set_one_stage(False)
+
+
 def run_gpu(inp, layer=None, x=None, valid=None):
     layer = layer or device_layer(inp)
     xd = (inp.x if x is None else x).cuda()

@@ -10,7 +10,8 @@ import oracle
 from workloads import get_config, make_inputs
 from workloads.gen import random_small
 
-from .parity import TOL, compare, device_layer, fp8_mfma, gemm_path, log, run_gpu
+from .parity import (TOL, compare, device_layer, fp8_mfma, gemm_path, log, one_stage,
+                     run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -215,21 +216,31 @@ def _gemm_capable(kw):
     return kw.get("act", "bf16") == "bf16" and kw["I"] % 128 == 0 and kw["H"] % 128 == 0
 
 
-@pytest.mark.parametrize("path", ["auto", "gemm", "gemm-fp8mfma"])
-@pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("i", range(len(SMALL)))
+def _small_cases():
+    """(layer, packed, path) combinations that apply: fp32 weights have no
+    packed layout; the GEMM paths need a shape the tiled kernels take; the fp8
+    MFMA setting only concerns fp8 weights."""
+    out = []
+    for i, kw in enumerate(SMALL):
+        for packed in (False, True):
+            if packed and kw.get("w") == "f32":
+                continue
+            for path in ("auto", "gemm", "gemm-fp8mfma"):
+                if path != "auto" and not _gemm_capable(kw):
+                    continue
+                if path == "gemm-fp8mfma" and kw.get("w") != "fp8":
+                    continue
+                out.append((i, packed, path))
+    return out
+
+
+@pytest.mark.parametrize("i,packed,path", _small_cases())
 def test_small_layers_match_oracle(i, packed, path):
     """path "gemm": segments above 16 rows take the tiled GEMM kernels (the
     others stream), so both expert paths meet in one call; "gemm-fp8mfma":
     the same with the fp8 MFMA on two-term token codes instead of fp8
     weights dequantised for bf16 MFMA."""
     kw = SMALL[i]
-    if packed and kw.get("w") == "f32":
-        pytest.skip("fp32 weights have no packed layout")
-    if path != "auto" and not _gemm_capable(kw):
-        pytest.skip("shape outside the tiled GEMM kernels")
-    if path == "gemm-fp8mfma" and kw.get("w") != "fp8":
-        pytest.skip("the fp8 MFMA setting only concerns fp8 weights")
     log(f"[case] small layer {i} packed={packed} path={path}: {kw}")
     inp = random_small(seed=100 + i, **kw)
     with fp8_mfma(path == "gemm-fp8mfma"):
@@ -266,19 +277,21 @@ def test_pack_weights_layout_bitwise(w):
     assert torch.equal(as_int(p2.cpu()), ref2)
 
 
-@pytest.mark.parametrize("kw", [
+_PACKED_CASES = [
     dict(T=300, H=1024, E=32, k=4, I=160, valid_frac=0.5),
     dict(T=400, H=512, E=4, k=2, I=256, w="fp8"),
     dict(T=200, H=384, E=8, k=2, I=128, n_shared=1),
     dict(T=300, H=256, E=4, k=2, I=384),
     dict(T=260, H=384, E=5, k=2, I=640, n_shared=1),
     dict(T=300, H=256, E=4, k=2, I=384, w="fp8"),
-])
-@pytest.mark.parametrize("path", ["auto", "gemm"])
+]
+
+
+@pytest.mark.parametrize("kw,path", [(kw, p) for kw in _PACKED_CASES for p in ("auto", "gemm")
+                                     if p == "auto" or _gemm_capable(kw)])
 def test_packed_weights_give_identical_output(kw, path):
-    """Only the weight addresses change with the layout: same bits out."""
-    if path == "gemm" and not _gemm_capable(kw):
-        pytest.skip("shape outside the tiled GEMM kernels")
+    """Only the weight addresses change with the layout: same bits out (the
+    GEMM path where the tiled kernels take the shape)."""
     inp = random_small(seed=11, **kw)
     with gemm_path() if path == "gemm" else contextlib.nullcontext():
         a = run_gpu(inp, device_layer(inp, packed=False))
@@ -388,6 +401,78 @@ def test_workload_matches_oracle(name, packed):
     gpu = run_gpu(inp, device_layer(inp, packed=packed))
     log(f"[case] {name}: oracle run")
     compare(inp, gpu)
+
+
+# The one-launch expert MLP (gate/up and down in one persistent launch, work
+# items taken from per-XCD queues, down units waiting on per-item counts) is
+# switched off and its kernel is not in the library: the first GPU run of its
+# first case (T=300, row-major weights) went silent until it was killed after
+# 180 s, and no cause has been found in its code.  The tests stay, skipped.
+ONE_STAGE_OFF = ("one-launch expert MLP switched off: its first GPU run hung and the "
+                 "cause is not found")
+
+ONE_STAGE_SMALL = [
+    dict(T=300, H=512, E=16, k=4, I=128, n_shared=1, valid_frac=0.7),
+    dict(T=64, H=512, E=8, k=2, I=256, w="fp8"),
+    dict(T=1, H=1024, E=4, k=1, I=128),
+    dict(T=200, H=512, E=3, k=2, I=384, w="fp8", n_shared=1),   # segments of several items
+    dict(T=40, H=512, E=64, k=8, I=128, n_shared=1),            # fewer items than XCD queues
+]
+
+
+@pytest.mark.skip(reason=ONE_STAGE_OFF)
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("kw", ONE_STAGE_SMALL)
+def test_one_stage_matches_two_launches(kw, packed):
+    """Gate/up and down in one launch (per-XCD work queues, h handed over
+    through one XCD's L2) give the two-launch path's bits, and the oracle's
+    values."""
+    inp = random_small(seed=91, **kw)
+    log(f"[case] one stage packed={packed}: {kw}")
+    ref = run_gpu(inp, device_layer(inp, packed=packed))
+    with one_stage(True):
+        gpu = run_gpu(inp, device_layer(inp, packed=packed))
+    assert np.array_equal(gpu["out"], ref["out"])
+    compare(inp, gpu)
+
+
+@pytest.mark.skip(reason=ONE_STAGE_OFF)
+@pytest.mark.parametrize("name", ["decode_e48", "decode_e256_shared"])
+def test_one_stage_decode_workloads(name):
+    cfg = get_config(name)
+    log(f"[case] one stage {name}")
+    inp = make_inputs(cfg)
+    ref = run_gpu(inp, device_layer(inp, packed=True))
+    with one_stage(True):
+        layer = device_layer(inp, packed=True)
+        gpu = run_gpu(inp, layer)
+        again = run_gpu(inp, layer)         # the sync words are reset by every call
+    assert np.array_equal(gpu["out"], ref["out"])
+    assert np.array_equal(again["out"], ref["out"])
+    compare(inp, gpu)
+
+
+@pytest.mark.skip(reason=ONE_STAGE_OFF)
+def test_one_stage_replays_in_a_hip_graph():
+    inp = random_small(seed=93, T=256, H=512, E=16, k=3, I=128, valid_frac=0.9)
+    with one_stage(True):
+        layer = device_layer(inp, packed=True)
+        xd = inp.x.cuda()
+        vd = inp.valid.cuda()
+        ref = layer.forward(xd, vd)
+        out = torch.empty_like(ref)
+        ws = layer.workspace(xd.shape[0])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.forward(xd, vd, out=out, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        assert torch.isfinite(junk)
 
 
 def test_gather_nan_padding_rows_are_never_read():
