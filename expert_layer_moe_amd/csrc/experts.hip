@@ -77,19 +77,24 @@ __device__ __forceinline__ int round_unit(int u0, int n_live) {
 
 // ---------------------------------------------------------------------------
 // Weight-streaming gate/up for expert segments of a few tiles of rows (the
-// decode regime, bound by HBM): one block per (work item, 4/KS groups of 16
-// intermediate columns), a work item being a segment and up to MT = 4 of its
-// 16-row tiles (the align's stream item table; a segment's items run side by
-// side, so its weights come from HBM once and are shared through L2).  The
-// block's waves split K = H into KS contiguous parts; a wave streams its part
-// of 16 gate rows and the 16 matching up rows of W13 once for the item's
-// tiles, issuing KU MFMA K-steps of loads ahead of their MFMAs.  Partial sums
-// of the KS waves meet in LDS (fixed order), then h = SiLU(g) * u in bf16.
-// Units: (item, column group), n_cg = ceil(I / (16 * 4 / KS)) per item.
-// bf16: three waves per SIMD (164 VGPRs, no spills) keep more weight loads in
-// flight; the fp8 variant keeps two (it would spill).
-template <int KS, int MT, int KU, bool FP8, bool PW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 ? 2 : 3)))
+// decode regime, bound by HBM): one block per (work item, column group), a
+// work item being a segment and up to MT = 4 of its 16-row tiles (the align's
+// stream item table; a segment's items run side by side, so its weights come
+// from HBM once and are shared through L2).  The block's waves split K = H
+// into KS contiguous parts; a wave streams its part of CGN 16-row tiles of
+// gate rows and the matching up rows of W13 once for the item's tiles,
+// issuing KU MFMA K-steps of loads ahead of their MFMAs.  Each token
+// fragment a wave loads feeds the MFMAs of its CGN column tiles.  The token
+// rows come from L2 once per column group; with one 16-column tile per wave
+// those L2 reads cost decode_e48 about a fifth of the kernel (167 us, 134
+// with them taken out in a timing copy), and two tiles per wave (CGN = 2,
+// two waves per SIMD, no spills) halve them: 157 us, gather_padded_e48 258
+// -> 240 us.  (Three or four tiles per wave: 153 / 179 us on decode_e48 but
+// 254 / 233 on gather_padded_e48.)  Partial sums of the KS waves meet in LDS
+// (fixed order, one column tile at a time), then h = SiLU(g) * u in bf16.
+// Units: (item, column group), n_cg = ceil(I / (16 CGN 4 / KS)) per item.
+template <int KS, int MT, int KU, int CGN, bool FP8, bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 || CGN > 1 ? 2 : 3)))
 void gate_up_stream_kernel(
     const uint16_t* __restrict__ xp, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
@@ -97,7 +102,7 @@ void gate_up_stream_kernel(
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
     uint16_t* __restrict__ h, int H, int I, int max_items, int n_cg) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
-  constexpr int CGW = 4 / KS;
+  constexpr int CGW = 4 / KS;   // waves side by side along the columns
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
   const int n_live = min(*n_items, max_items) * n_cg;
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
@@ -109,30 +114,38 @@ void gate_up_stream_kernel(
     const int row0 = seg_off[e];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int ks = wave % KS, cw = wave / KS;
-    const int cg = cgb * CGW + cw;
-    const bool col_ok = cg * 16 < I;
     const int m = lane % 16, g = lane / 16;
     const int klen = H / KS, kbeg = ks * klen;
-    const int c0 = col_ok ? cg * 16 : 0;
-    // this lane's element offset in the gate / up rows at step 0 of its K
+    // the wave's column tiles j: columns c0[j] .. + 15 (a tile past I is
+    // neither loaded nor stored)
+    bool col_ok[CGN];
+    int c0[CGN];
+    // this lane's element offsets in the gate / up rows at step 0 of its K
     // part, and the distance of one MFMA K step (row-major: 32 elements along
     // the row; fragment-packed: the next 512-element block of the same tile)
     constexpr size_t wstep = PW ? 512 : 32;
-    size_t wg_off, wu_off;
-    if constexpr (PW) {
-      const size_t tg = ((size_t)e * 2 * I + c0) / 16, tu = tg + I / 16;
-      wg_off = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-      wu_off = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-    } else {
-      wg_off = ((size_t)e * 2 * I + c0 + m) * H + kbeg + 8 * g;
-      wu_off = wg_off + (size_t)I * H;
-    }
-    const float* sg = nullptr;
-    const float* su = nullptr;
-    if constexpr (FP8) {
-      const int nkb = H / 128;
-      sg = s13 + ((size_t)e * (2 * I / 128) + c0 / 128) * nkb;
-      su = s13 + ((size_t)e * (2 * I / 128) + (I + c0) / 128) * nkb;
+    size_t wg_off[CGN], wu_off[CGN];
+    const float* sg[CGN];
+    const float* su[CGN];
+#pragma unroll
+    for (int j = 0; j < CGN; ++j) {
+      const int c = ((cgb * CGW + cw) * CGN + j) * 16;
+      col_ok[j] = c < I;
+      c0[j] = col_ok[j] ? c : 0;
+      if constexpr (PW) {
+        const size_t tg = ((size_t)e * 2 * I + c0[j]) / 16, tu = tg + I / 16;
+        wg_off[j] = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+        wu_off[j] = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+      } else {
+        wg_off[j] = ((size_t)e * 2 * I + c0[j] + m) * H + kbeg + 8 * g;
+        wu_off[j] = wg_off[j] + (size_t)I * H;
+      }
+      sg[j] = su[j] = nullptr;
+      if constexpr (FP8) {
+        const int nkb = H / 128;
+        sg[j] = s13 + ((size_t)e * (2 * I / 128) + c0[j] / 128) * nkb;
+        su[j] = s13 + ((size_t)e * (2 * I / 128) + (I + c0[j]) / 128) * nkb;
+      }
     }
     const u32x4 zero = {0u, 0u, 0u, 0u};
     // the item's 16-row tiles [tb, te) of the segment
@@ -144,101 +157,128 @@ void gate_up_stream_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
-      floatx4 ag[MT], au[MT];
+      floatx4 ag[CGN][MT], au[CGN][MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        ag[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        au[mt] = ag[mt];
-      }
-      if (col_ok) {
+      for (int j = 0; j < CGN; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          ag[j][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          au[j][mt] = ag[j][mt];
+        }
+      // W13 of a segment with one item is read by this block alone:
+      // non-temporal loads (measured faster on the decode batches); the items
+      // of a larger segment share it through L2 (normal loads measured faster)
+      auto k_loop = [&](auto nt_tag) {
+        constexpr bool kNT = decltype(nt_tag)::value;
         for (int kk = 0; kk < klen; kk += 32 * KU) {
-          bf16x8 bg[KU], bu[KU], a[KU][MT];
+          bf16x8 bg[KU][CGN], bu[KU][CGN], a[KU][MT];
 #pragma unroll
-          for (int u = 0; u < KU; ++u) {
-            bg[u] = load_w8<FP8>(w13, wg_off + (size_t)(kk / 32 + u) * wstep);
-            bu[u] = load_w8<FP8>(w13, wu_off + (size_t)(kk / 32 + u) * wstep);
-          }
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int j = 0; j < CGN; ++j) {
+              if (j == 0 || col_ok[j]) {
+                bg[u][j] = load_w8<FP8, kNT>(w13, wg_off[j] + (size_t)(kk / 32 + u) * wstep);
+                bu[u][j] = load_w8<FP8, kNT>(w13, wu_off[j] + (size_t)(kk / 32 + u) * wstep);
+              } else {
+                bg[u][j] = bu[u][j] = as_bf16x8(zero);
+              }
+            }
 #pragma unroll
           for (int u = 0; u < KU; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
               a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
           if constexpr (FP8) {
-            floatx4 pg[MT], pu[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-              pu[mt] = pg[mt];
-            }
+            for (int j = 0; j < CGN; ++j) {
+              floatx4 pg[MT], pu[MT];
 #pragma unroll
-            for (int u = 0; u < KU; ++u)
+              for (int mt = 0; mt < MT; ++mt) {
+                pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                pu[mt] = pg[mt];
+              }
+#pragma unroll
+              for (int u = 0; u < KU; ++u)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  if (t0 + mt < te) {
+                    pg[mt] = mfma16x16x32(a[u][mt], bg[u][j], pg[mt]);
+                    pu[mt] = mfma16x16x32(a[u][mt], bu[u][j], pu[mt]);
+                  }
+              const int kb = (kbeg + kk) >> 7;
+              const float scg = sg[j][kb], scu = su[j][kb];
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                if (t0 + mt < te) {
-                  pg[mt] = mfma16x16x32(a[u][mt], bg[u], pg[mt]);
-                  pu[mt] = mfma16x16x32(a[u][mt], bu[u], pu[mt]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  ag[j][mt][i] = fmaf(scg, pg[mt][i], ag[j][mt][i]);
+                  au[j][mt][i] = fmaf(scu, pu[mt][i], au[j][mt][i]);
                 }
-            const int kb = (kbeg + kk) >> 7;
-            const float scg = sg[kb], scu = su[kb];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                ag[mt][i] = fmaf(scg, pg[mt][i], ag[mt][i]);
-                au[mt][i] = fmaf(scu, pu[mt][i], au[mt][i]);
-              }
+            }
           } else {
 #pragma unroll
             for (int u = 0; u < KU; ++u)
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                if (t0 + mt < te) {
-                  ag[mt] = mfma16x16x32(a[u][mt], bg[u], ag[mt]);
-                  au[mt] = mfma16x16x32(a[u][mt], bu[u], au[mt]);
-                }
+                if (t0 + mt < te)
+#pragma unroll
+                  for (int j = 0; j < CGN; ++j) {
+                    ag[j][mt] = mfma16x16x32(a[u][mt], bg[u][j], ag[j][mt]);
+                    au[j][mt] = mfma16x16x32(a[u][mt], bu[u][j], au[j][mt]);
+                  }
           }
         }
+      };
+      // (fragment-packed weights only, as for W2 in the down kernel)
+      if (col_ok[0]) {
+        if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
+        else k_loop(std::false_type{});
       }
-      if constexpr (KS == 1) {
-        if (col_ok) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
+      for (int j = 0; j < CGN; ++j) {
+        if constexpr (KS == 1) {
+          if (col_ok[j]) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = (t0 + mt) * 16 + 4 * g + i;
-              if (r < cnt)
-                h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(ag[mt][i], au[mt][i]));
-            }
-        }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          red[wave][0][mt][lane] = ag[mt];
-          red[wave][1][mt][lane] = au[mt];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if ((mt % KS) == ks && t0 + mt < te && col_ok) {
-            floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
-#pragma unroll
-            for (int q = 1; q < KS; ++q) {
-              const floatx4 g2 = red[cw * KS + q][0][mt][lane];
-              const floatx4 u2 = red[cw * KS + q][1][mt][lane];
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                G[i] += g2[i];
-                U[i] += u2[i];
+                const int r = (t0 + mt) * 16 + 4 * g + i;
+                if (r < cnt)
+                  h[frag_index(row0 + r, c0[j] + m, I)] =
+                      f32_to_bf16_bits(silu_mul(ag[j][mt][i], au[j][mt][i]));
+              }
+          }
+        } else {
+          // column tile j of every wave through the one LDS buffer
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            red[wave][0][mt][lane] = ag[j][mt];
+            red[wave][1][mt][lane] = au[j][mt];
+          }
+          __syncthreads();
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            if ((mt % KS) == ks && t0 + mt < te && col_ok[j]) {
+              floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
+#pragma unroll
+              for (int q = 1; q < KS; ++q) {
+                const floatx4 g2 = red[cw * KS + q][0][mt][lane];
+                const floatx4 u2 = red[cw * KS + q][1][mt][lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  G[i] += g2[i];
+                  U[i] += u2[i];
+                }
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int r = (t0 + mt) * 16 + 4 * g + i;
+                if (r < cnt) h[frag_index(row0 + r, c0[j] + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
               }
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = (t0 + mt) * 16 + 4 * g + i;
-              if (r < cnt) h[frag_index(row0 + r, c0 + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
-            }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
   }
@@ -417,6 +457,9 @@ int pick_ku(int len) {
   return 1;
 }
 
+// 16-column tiles per wave of the streaming gate/up (the kernel's CGN)
+constexpr int kGuCgn = 2;
+
 struct GuArgs {
   dim3 grid;
   hipStream_t s;
@@ -434,7 +477,7 @@ struct GuArgs {
 
 template <int KS, int KU, bool FP8, bool PW>
 void launch_gu(const GuArgs& a) {
-  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s,
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, kGuCgn, FP8, PW>), a.grid, dim3(256), 0, a.s,
                      a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0,
                      a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg);
 }
@@ -518,7 +561,7 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   int ks = 4;
   while (ks > 1 && (H % ks != 0 || (H / ks) % (fp8 ? 128 : 32) != 0)) ks >>= 1;
   const int ku = pick_ku(H / ks);
-  const int cgw = 4 / ks;
+  const int cgw = 4 / ks * kGuCgn;   // 16-column tiles per block
   const int n_cg = (I / 16 + cgw - 1) / cgw;
   if (bm % 16 != 0 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
   GuArgs a{dim3(stream_grid(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
