@@ -287,8 +287,13 @@ void gate_up_stream_kernel(
 // Weight-streaming down projection: one block per (work item, 64*NT output
 // columns); each wave streams NT 16-row tiles of W2 (full K = I) once for
 // the item's (up to MT) 16-row tiles of h.  W2 is the MFMA's A operand, so
-// a lane ends with 4 consecutive output columns of one row, stored as one
-// piece of the row's y (16 bytes of fp32, or 8 of bf16 with fp8 weights).
+// a lane ends with 4 consecutive output columns of one row.  Written as they
+// are, a store instruction would cover 16 rows x 64 bytes: every 128-byte
+// line of y in two halves from different instructions, which cost decode_e48
+// 16 us of its 91 (90.6 -> 74.2 us with the stores taken out in a timing
+// copy).  So each wave passes its 16 x 64 tile through its own LDS rows
+// first, and a store instruction writes 4 whole rows of the tile (4 x 256
+// bytes of fp32, or 4 x 128 of bf16 with fp8 weights).
 // Units: (item, column group), n_ng = ceil(H / (64 * NT)) per item (NT = 4).
 template <int MT, int NT, int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(256) void down_stream_kernel(
@@ -298,6 +303,10 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
     void* __restrict__ y, int H, int I, int max_items, int n_ng) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
+  static_assert(NT == 4, "the store pass moves 64-column tiles");
+  // per wave: one 16-row x 64-column tile of y on its way out (rows padded
+  // to 68 floats against bank conflicts); only its own wave touches it
+  __shared__ floatx4 ytile[4][16][17];
   const int n_live = min(*n_items, max_items) * n_ng;
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
     const int lid = round_unit(u0, n_live);
@@ -389,15 +398,22 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
       // 128-byte line, and the next step needs the line again)
       if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
       else k_loop(std::false_type{});
-      // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt + 4 g .. + 3
+      // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt +
+      // 4 g .. + 3.  Through LDS: lane l then holds row 4 q + l / 16 of the
+      // tile, columns n0 + 4 (l % 16) .. + 3, for q = 0 .. 3.
+      const int lr = lane / 16, lc = lane % 16;
+      const bool col_in = n0 + 4 * lc < H;   // H is a multiple of 16
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const int r = (t0 + mt) * 16 + m;
-        if (r >= cnt) continue;
+        if (t0 + mt >= te) continue;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (n0 + nt * 16 >= H) continue;
-          store_y4<FP8>(y, (size_t)(row0 + r) * H + n0 + nt * 16 + 4 * g, acc[mt][nt]);
+        for (int nt = 0; nt < NT; ++nt) ytile[wave][m][4 * nt + g] = acc[mt][nt];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tr = 4 * q + lr;
+          const int r = (t0 + mt) * 16 + tr;
+          const floatx4 v = ytile[wave][tr][lc];
+          if (r < cnt && col_in) store_y4<FP8>(y, (size_t)(row0 + r) * H + n0 + 4 * lc, v);
         }
       }
     }
