@@ -473,7 +473,9 @@ int pick_ku(int len) {
   return 1;
 }
 
-// 16-column tiles per wave of the streaming gate/up (the kernel's CGN)
+// 16-column tiles per wave of the streaming gate/up (the kernel's CGN) with
+// fragment-packed weights; row-major weights keep one (their 16-row x 64-byte
+// loads: decode_e48 gate/up 198 us with one, 204 with two)
 constexpr int kGuCgn = 2;
 
 struct GuArgs {
@@ -493,7 +495,7 @@ struct GuArgs {
 
 template <int KS, int KU, bool FP8, bool PW>
 void launch_gu(const GuArgs& a) {
-  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, kGuCgn, FP8, PW>), a.grid, dim3(256), 0, a.s,
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, PW ? kGuCgn : 1, FP8, PW>), a.grid, dim3(256), 0, a.s,
                      a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0,
                      a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg);
 }
@@ -577,7 +579,7 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   int ks = 4;
   while (ks > 1 && (H % ks != 0 || (H / ks) % (fp8 ? 128 : 32) != 0)) ks >>= 1;
   const int ku = pick_ku(H / ks);
-  const int cgw = 4 / ks * kGuCgn;   // 16-column tiles per block
+  const int cgw = 4 / ks * (packed ? kGuCgn : 1);   // 16-column tiles per block
   const int n_cg = (I / 16 + cgw - 1) / cgw;
   if (bm % 16 != 0 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
   GuArgs a{dim3(stream_grid(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
