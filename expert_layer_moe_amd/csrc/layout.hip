@@ -290,8 +290,14 @@ hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const 
     return hipGetLastError();
   }
   const float* yf = static_cast<const float*>(y);
-  // two 4-column groups per thread once there are rows enough to fill the chip
-  if (T >= 256)
+  // two 4-column groups per thread once there are rows enough to fill the
+  // chip; on large batches one block per row (up to 8192 columns): a quarter
+  // of the blocks, each with 4x the loads in flight (gather_padded_e48, 86%
+  // padding rows that only take zeros: 57.8 -> 50.5 us)
+  if (T >= 2048)
+    hipLaunchKernelGGL(combine_kernel<8>, dim3(T, (H + 8191) / 8192), dim3(256), 0, s, yf, ids,
+                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  else if (T >= 256)
     hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, yf, ids,
                        w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
   else
