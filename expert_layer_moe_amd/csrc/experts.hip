@@ -170,7 +170,15 @@ void gate_up_stream_kernel(
       // of a larger segment share it through L2 (normal loads measured faster)
       auto k_loop = [&](auto nt_tag) {
         constexpr bool kNT = decltype(nt_tag)::value;
-        for (int kk = 0; kk < klen; kk += 32 * KU) {
+        // The blocks of one item read the same token rows; started at the
+        // same K they would all ask the same L2 lines at once.  Each group of
+        // 32 columns starts its K loop at its own batch (a fixed order per
+        // column, so the sums do not depend on the block shape): decode_e48
+        // gate/up 157 -> 149 us.
+        const int nbat = klen / (32 * KU);
+        const int rot = (c0[0] / 32) % nbat * (32 * KU);
+        for (int kk0 = 0; kk0 < klen; kk0 += 32 * KU) {
+          const int kk = kk0 + rot < klen ? kk0 + rot : kk0 + rot - klen;
           bf16x8 bg[KU][CGN], bu[KU][CGN], a[KU][MT];
 #pragma unroll
           for (int u = 0; u < KU; ++u)
