@@ -9,6 +9,8 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -17,17 +19,14 @@ namespace {
 // of the memory system to the weight stream.  The down projection's input h
 // is written in the same order by the gate/up kernel.
 //
-// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15, for the tiles of
-// segments left to the streaming kernels.  Padding rows are not written: an
-// MFMA keeps the rows of its token operand apart, so whatever they hold only
-// reaches output rows that are never stored.
-// grid = (cap / 16, chunks of kpc steps); the sorted list's blocks (of the
-// segments' padding granularity) hold tiles_per_block 16-row tiles.
+// xp tile t = x rows of the sorted rows 16 t .. 16 t + 15.  Padding rows are
+// not written: an MFMA keeps the rows of its token operand apart, so whatever
+// they hold only reaches output rows that are never stored.
+// This kernel serves calls where every segment streams (no tiled GEMM):
+// grid = (cap / 16, chunks of kpc steps).
 __global__ __launch_bounds__(256) void pack_x_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ n_post,
-    const int32_t* __restrict__ seg_cnt, int big_thr, const int32_t* __restrict__ gemm_tiles,
-    uint16_t* __restrict__ xp, int H, int k, int kpc, int tiles_per_block) {
+    const int32_t* __restrict__ n_post, uint16_t* __restrict__ xp, int H, int k, int kpc) {
   const int tile = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int m = lane % 16, g = lane / 16;
@@ -36,9 +35,6 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
   // loads matters in a kernel this small
   const int sid = sorted_ids[tile * 16 + m];
   if (tile * 16 >= *n_post) return;
-  if (gemm_tiles != nullptr && seg_cnt[block_expert[tile / tiles_per_block]] > big_thr &&
-      *gemm_tiles > 0)
-    return;
   const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
   uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
   const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
@@ -46,6 +42,40 @@ __global__ __launch_bounds__(256) void pack_x_kernel(
 #pragma unroll 8
   for (int s = s0 + wave; s < s1; s += 4)
     *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = ld16(src + 32 * s);
+}
+
+// The same packing driven by the streaming kernels' item table, for calls
+// where the tiled GEMM may take the large segments: the work is then the
+// items of the few streaming segments, while a grid over every 16-row tile
+// of the sorted list spent the prefill micro-batch's 14 us mostly on blocks
+// that found their tile on the GEMM path.  Units (item, 16-row tile of the
+// item, chunk of kpc K steps), looped over by a capped grid.
+__global__ __launch_bounds__(256) void pack_x_items_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    const int32_t* __restrict__ item_seg, const int32_t* __restrict__ item_row0,
+    const int32_t* __restrict__ n_items, int max_items, uint16_t* __restrict__ xp, int H,
+    int k, int kpc, int n_kc) {
+  constexpr int kTiles = kStreamItemRows / 16;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int m = lane % 16, g = lane / 16;
+  const int n_units = min(*n_items, max_items) * kTiles * n_kc;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int item = u / (kTiles * n_kc), rest = u - item * (kTiles * n_kc);
+    const int tt = rest / n_kc, kc = rest - tt * n_kc;
+    const int e = item_seg[item];
+    const int r0 = item_row0[item] + 16 * tt;   // first row of the tile in its segment
+    if (r0 >= seg_cnt[e]) continue;
+    const int tile = (seg_off[e] + r0) / 16;    // segments start on 16-row boundaries
+    const int sid = sorted_ids[tile * 16 + m];
+    if (sid < 0) continue;                      // a padding row of the segment
+    const uint16_t* src = x + (size_t)(sid / k) * H + 8 * g;
+    uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
+    const int s0 = kc * kpc, s1 = min(H / 32, s0 + kpc);
+#pragma unroll 8
+    for (int s = s0 + wave; s < s1; s += 4)
+      *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = ld16(src + 32 * s);
+  }
 }
 
 // Token rows as two e4m3 terms for the fp8-MFMA gate/up GEMM: with one
@@ -242,16 +272,30 @@ __global__ __launch_bounds__(256) void combine_ybf_kernel(
 
 }  // namespace
 
-hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
-                         const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
-                         const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
-                         int max_rows, hipStream_t s) {
-  if (bm % 16 != 0 || H % 32 != 0 || max_rows % 16 != 0) return hipErrorInvalidValue;
+hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* n_post,
+                         void* xp, int H, int k, int max_rows, hipStream_t s) {
+  if (H % 32 != 0 || max_rows % 16 != 0) return hipErrorInvalidValue;
   const int kpc = 32;   // MFMA steps per block
   hipLaunchKernelGGL(pack_x_kernel, dim3(max_rows / 16, (H / 32 + kpc - 1) / kpc), dim3(256), 0,
-                     s, static_cast<const uint16_t*>(x), sorted_ids, block_expert, n_post,
-                     seg_cnt, big_thr, gemm_tiles, static_cast<uint16_t*>(xp), H, k, kpc,
-                     bm / 16);
+                     s, static_cast<const uint16_t*>(x), sorted_ids, n_post,
+                     static_cast<uint16_t*>(xp), H, k, kpc);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_x_items(const void* x, const int32_t* sorted_ids, const int32_t* seg_off,
+                               const int32_t* seg_cnt, const int32_t* item_seg,
+                               const int32_t* item_row0, const int32_t* n_items, int max_items,
+                               void* xp, int H, int k, hipStream_t s) {
+  if (H % 32 != 0 || max_items < 0) return hipErrorInvalidValue;
+  const int kpc = 32;   // MFMA steps per unit
+  const int n_kc = (H / 32 + kpc - 1) / kpc;
+  // the largest grid the chip holds at once, or less when fewer units can exist
+  constexpr int kPackItemsGrid = 2048;
+  const long long bound = (long long)max_items * (kStreamItemRows / 16) * n_kc;
+  const int grid = (int)std::max(1LL, std::min<long long>(bound, kPackItemsGrid));
+  hipLaunchKernelGGL(pack_x_items_kernel, dim3(grid), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), sorted_ids, seg_off, seg_cnt, item_seg,
+                     item_row0, n_items, max_items, static_cast<uint16_t*>(xp), H, k, kpc, n_kc);
   return hipGetLastError();
 }
 

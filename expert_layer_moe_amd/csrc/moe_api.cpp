@@ -278,9 +278,11 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
   }
   if (wkind != moe::W_F32) {
     StageTimer tm(S_PACK_X, s);
-    if (moe::launch_pack_x(x, sorted, bexp, npost, cnt, p.big_thr, gemm ? ntiles : nullptr, y,
-                           p.H, p.k, p.bm, p.cap, s) != hipSuccess)
-      return MOE_ERR_HIP;
+    const hipError_t e =
+        gemm ? moe::launch_pack_x_items(x, sorted, offs, cnt, iseg, irow, nitems, p.max_items, y,
+                                        p.H, p.k, s)
+             : moe::launch_pack_x(x, sorted, npost, y, p.H, p.k, p.cap, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_GATE_UP, s);

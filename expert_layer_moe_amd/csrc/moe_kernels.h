@@ -58,13 +58,17 @@ inline int max_stream_items(long long n_rows, int nseg) {
 // their per-block table of 128-wide scale blocks).
 constexpr int kMaxGemmK = 16384;
 
-// bf16 streaming path: x rows of the sorted rows of the streaming kernels'
-// segments, packed in MFMA fragment order into xp (max_rows x H bf16, 16-row
-// tiles; padding rows 0).  bm (the segments' padding) is a multiple of 16.
-hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* block_expert,
-                         const int32_t* n_post, const int32_t* seg_cnt, int big_thr,
-                         const int32_t* gemm_tiles, void* xp, int H, int k, int bm,
-                         int max_rows, hipStream_t s);
+// bf16 streaming path, calls without the tiled GEMM: x rows of the sorted
+// rows (the first *n_post of max_rows), packed in MFMA fragment order into xp
+// (max_rows x H bf16, 16-row tiles; padding rows left as they are).
+hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* n_post,
+                         void* xp, int H, int k, int max_rows, hipStream_t s);
+// The same packing for calls where the tiled GEMM may run: only the rows of
+// the stream item table's items (the streaming segments) are packed.
+hipError_t launch_pack_x_items(const void* x, const int32_t* sorted_ids, const int32_t* seg_off,
+                               const int32_t* seg_cnt, const int32_t* item_seg,
+                               const int32_t* item_row0, const int32_t* n_items, int max_items,
+                               void* xp, int H, int k, hipStream_t s);
 // h[r, :] = SiLU(W_gate x_tok(r)) * (W_up x_tok(r)) for the sorted rows of
 // the stream item table (item_seg, item_row0: a segment and the first of up
 // to 64 of its rows; *n_items of them, at most max_items; segments at
