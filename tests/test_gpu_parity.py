@@ -403,6 +403,21 @@ def test_workload_matches_oracle(name, packed):
     compare(inp, gpu)
 
 
+def test_prefill_fp8_mfma_two_term_matches_oracle():
+    """The prefill micro-batch with its tiled gate/up on the fp8 MFMA over the
+    two-term e4m3 token codes (the moe_set_fp8_mfma option): the oracle's
+    values within the fp8 bar, at the full size."""
+    cfg = get_config("prefill_ub_fp8")
+    log("[case] prefill_ub_fp8 fp8 MFMA two-term: generating inputs")
+    inp = make_inputs(cfg)
+    with fp8_mfma(True):
+        layer = device_layer(inp, packed=True)
+        log("[case] prefill_ub_fp8 fp8 MFMA two-term: GPU run")
+        gpu = run_gpu(inp, layer)
+    log("[case] prefill_ub_fp8 fp8 MFMA two-term: oracle run")
+    compare(inp, gpu)
+
+
 # The one-launch expert MLP (gate/up and down in one persistent launch, work
 # items taken from per-XCD queues, down units waiting on per-item counts) is
 # switched off and its kernel is not in the library: the first GPU run of its
