@@ -14,7 +14,7 @@ MFMA-bound half of the metric), the two micro-batches on two HIP streams,
 the unsplit 16384-row batch and the request-boundary split (7003 / 9381),
 and the tiny fp32 correctness layer.  Prints one JSON line.
 
-Other modes (profiling runs, not used by the driver):
+Other modes (profiling runs; the default run takes none of them):
   --config NAME       only that workload (tiny, decode_e48, decode_e256_shared,
                       gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8,
                       prefill_unsplit, prefill_boundary_split)
