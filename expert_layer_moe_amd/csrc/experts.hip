@@ -89,8 +89,8 @@ __device__ __forceinline__ int round_unit(int u0, int n_live) {
 // those L2 reads cost decode_e48 about a fifth of the kernel (167 us, 134
 // with them taken out in a timing copy), and two tiles per wave (CGN = 2,
 // two waves per SIMD, no spills) halve them: 157 us, gather_padded_e48 258
-// -> 240 us.  (Three or four tiles per wave: 153 / 179 us on decode_e48 but
-// 254 / 233 on gather_padded_e48.)  Partial sums of the KS waves meet in LDS
+// -> 240 us.  (Three or four tiles per wave: 179 / 153 us on decode_e48 but
+// 233 / 254 on gather_padded_e48.)  Partial sums of the KS waves meet in LDS
 // (fixed order, one column tile at a time), then h = SiLU(g) * u in bf16.
 // Units: (item, column group), n_cg = ceil(I / (16 CGN 4 / KS)) per item.
 template <int KS, int MT, int KU, int CGN, bool FP8, bool PW>
