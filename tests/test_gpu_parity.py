@@ -209,6 +209,9 @@ SMALL = [
     dict(T=300, H=256, E=4, k=2, I=384),
     dict(T=260, H=384, E=5, k=2, I=640, n_shared=1),
     dict(T=300, H=256, E=4, k=2, I=384, w="fp8"),
+    # a large batch (one combine block per row) with H past 8192 columns and
+    # not a multiple of 256 (the down kernel's last column group half used)
+    dict(T=2100, H=8320, E=8, k=2, I=64, valid_frac=0.6),
 ]
 
 
