@@ -303,7 +303,9 @@ void gate_up_stream_kernel(
 // first, and a store instruction writes 4 whole rows of the tile (4 x 256
 // bytes of fp32, or 4 x 128 of bf16 with fp8 weights).
 // Units: (item, column group), n_ng = ceil(H / (64 * NT)) per item (NT = 4).
-template <int MT, int NT, int KU, bool FP8, bool PW>
+// Y24: y rows as 24-bit floats (bf16-weight calls where every segment
+// streams; the writes of y are what the kernel pays most for besides W2).
+template <int MT, int NT, int KU, bool FP8, bool PW, bool Y24>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
@@ -421,7 +423,11 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
           const int tr = 4 * q + lr;
           const int r = (t0 + mt) * 16 + tr;
           const floatx4 v = ytile[wave][tr][lc];
-          if (r < cnt && col_in) store_y4<FP8>(y, (size_t)(row0 + r) * H + n0 + 4 * lc, v);
+          if (r < cnt && col_in) {
+            const size_t yi = (size_t)(row0 + r) * H + n0 + 4 * lc;
+            if constexpr (Y24) store_y24(y, yi, v);
+            else store_y4<FP8>(y, yi, v);
+          }
         }
       }
     }
@@ -544,18 +550,18 @@ struct DnArgs {
   int H, I, max_items, n_ng;
 };
 
-template <int KU, bool FP8, bool PW>
+template <int KU, bool FP8, bool PW, bool Y24>
 void launch_dn(const DnArgs& a) {
-  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
+  hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW, Y24>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
                      a.s2, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0, a.n_items, a.y, a.H,
                      a.I, a.max_items, a.n_ng);
 }
 
-template <bool FP8, bool PW>
+template <bool FP8, bool PW, bool Y24 = false>
 void launch_dn_ku(int ku, const DnArgs& a) {
-  if (ku == 4) launch_dn<4, FP8, PW>(a);
-  else if (ku == 2) launch_dn<2, FP8, PW>(a);
-  else launch_dn<1, FP8, PW>(a);
+  if (ku == 4) launch_dn<4, FP8, PW, Y24>(a);
+  else if (ku == 2) launch_dn<2, FP8, PW, Y24>(a);
+  else launch_dn<1, FP8, PW, Y24>(a);
 }
 
 int round8(int v) { return (v + 7) / 8 * 8; }
@@ -608,7 +614,7 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
-                       int bm, int max_rows, hipStream_t s) {
+                       int bm, int max_rows, bool y24, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
@@ -625,8 +631,13 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
     if (packed) launch_dn_ku<true, true>(ku, a);
     else launch_dn_ku<true, false>(ku, a);
   } else {
-    if (packed) launch_dn_ku<false, true>(ku, a);
-    else launch_dn_ku<false, false>(ku, a);
+    if (y24) {
+      if (packed) launch_dn_ku<false, true, true>(ku, a);
+      else launch_dn_ku<false, false, true>(ku, a);
+    } else {
+      if (packed) launch_dn_ku<false, true>(ku, a);
+      else launch_dn_ku<false, false>(ku, a);
+    }
   }
   return hipGetLastError();
 }

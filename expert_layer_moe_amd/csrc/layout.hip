@@ -180,10 +180,10 @@ __device__ __forceinline__ bool combine_slots(const int32_t* ids, const float* w
   return valid;
 }
 
-// fp32 y rows (y is read once: non-temporal loads)
-template <int NV>
+// fp32 y rows, or 24-bit ones (Y24); y is read once: non-temporal loads
+template <int NV, bool Y24>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const float* __restrict__ y, const int32_t* __restrict__ ids,
+    const void* __restrict__ y, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
     int H, int k, int ns, void* __restrict__ out, int out_bf16) {
   const int t = blockIdx.x;
@@ -207,8 +207,14 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
           if (n[v] < H) {
-            const floatx4 val = __builtin_nontemporal_load(
-                reinterpret_cast<const floatx4*>(y + (size_t)pos[j] * H + n[v]));
+            const size_t yi = (size_t)pos[j] * H + n[v];
+            floatx4 val;
+            if constexpr (Y24)
+              val = unpack_y24(__builtin_nontemporal_load(
+                  reinterpret_cast<const u32x3*>(static_cast<const uint8_t*>(y) + yi * 3)));
+            else
+              val = __builtin_nontemporal_load(
+                  reinterpret_cast<const floatx4*>(static_cast<const float*>(y) + yi));
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[v][i] = fmaf(wt[j], val[i], acc[v][i]);
           }
@@ -322,31 +328,35 @@ hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t row
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const float* w,
+hipError_t launch_combine(const void* y, int yfmt, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s) {
-  if (y_bf16) {
+  if (yfmt == Y_BF16) {
     if (!out_bf16 || H % 8 != 0) return hipErrorInvalidValue;
     hipLaunchKernelGGL(combine_ybf_kernel, dim3(T, (H + 2047) / 2048), dim3(256), 0, s,
                        static_cast<const uint16_t*>(y), ids, w, slot_pos, H, k, n_shared,
                        static_cast<uint16_t*>(out));
     return hipGetLastError();
   }
-  const float* yf = static_cast<const float*>(y);
+  if (yfmt != Y_F32 && yfmt != Y_F24) return hipErrorInvalidValue;
   // two 4-column groups per thread once there are rows enough to fill the
   // chip; on large batches one block per row (up to 8192 columns): a quarter
   // of the blocks, each with 4x the loads in flight (gather_padded_e48, 86%
   // padding rows that only take zeros: 57.8 -> 50.5 us)
-  if (T >= 2048)
-    hipLaunchKernelGGL(combine_kernel<8>, dim3(T, (H + 8191) / 8192), dim3(256), 0, s, yf, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
-  else if (T >= 256)
-    hipLaunchKernelGGL(combine_kernel<2>, dim3(T, (H + 2047) / 2048), dim3(256), 0, s, yf, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
-  else
-    hipLaunchKernelGGL(combine_kernel<1>, dim3(T, (H + 1023) / 1024), dim3(256), 0, s, yf, ids,
-                       w, slot_pos, T, H, k, n_shared, out, out_bf16 ? 1 : 0);
+  const int ob = out_bf16 ? 1 : 0;
+#define MOE_COMBINE(NV, Y24)                                                                  \
+  hipLaunchKernelGGL((combine_kernel<NV, Y24>), dim3(T, (H + 1024 * NV - 1) / (1024 * NV)),    \
+                     dim3(256), 0, s, y, ids, w, slot_pos, T, H, k, n_shared, out, ob)
+  const bool y24 = yfmt == Y_F24;
+  if (T >= 2048) {
+    if (y24) MOE_COMBINE(8, true); else MOE_COMBINE(8, false);
+  } else if (T >= 256) {
+    if (y24) MOE_COMBINE(2, true); else MOE_COMBINE(2, false);
+  } else {
+    if (y24) MOE_COMBINE(1, true); else MOE_COMBINE(1, false);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

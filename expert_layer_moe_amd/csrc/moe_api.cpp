@@ -33,6 +33,7 @@ struct Plan {
       off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_iseg, off_irow, off_nitems,
       off_span, off_h, off_y, off_xq, off_sx, total;
   bool xsplit;    // fp8 weights on the GEMM path: token rows as two e4m3 terms
+  int yfmt;       // format of the expert output rows y (moe::YFmt)
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -167,8 +168,14 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->off_nitems = take(4);
   p->off_span = take((size_t)moe::align_spans(p->T, p->k, p->ns) * (p->E + p->ns) * 4);
   p->off_h = take((size_t)p->cap * p->I * act_h);
-  // y rows (fp32; bf16 with fp8 weights) also hold the packed token rows of
-  // the streaming gate/up (cap x H bf16) until the down kernels overwrite them
+  // y rows: bf16 with fp8 weights; with bf16 weights 24-bit floats when
+  // every segment streams (only the streaming down kernel writes them), fp32
+  // otherwise.  The room is that of fp32 rows with bf16 weights whatever the
+  // format, so that the workspace size does not depend on the path
+  // thresholds.  It also holds the packed token rows of the streaming
+  // gate/up (cap x H bf16) until the down kernels overwrite them.
+  p->yfmt = p->w == MOE_FP8_E4M3 ? moe::Y_BF16
+            : (p->w == MOE_BF16 && p->big_thr == INT_MAX) ? moe::Y_F24 : moe::Y_F32;
   p->off_y = take((size_t)p->cap * p->H * (p->w == MOE_FP8_E4M3 ? 2 : 4));
   // two e4m3 code planes of the token rows and their scales (fp8 MFMA path):
   // room whenever the shape can take the tiled GEMM (so the workspace size
@@ -307,7 +314,7 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
   {
     StageTimer tm(S_DOWN, s);
     if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
-                         irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap,
+                         irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap, p.yfmt == moe::Y_F24,
                          s) != hipSuccess)
       return MOE_ERR_HIP;
   }
@@ -319,7 +326,7 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
   }
   {
     StageTimer tm(S_COMBINE, s);
-    if (moe::launch_combine(y, p.w == MOE_FP8_E4M3, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+    if (moe::launch_combine(y, p.yfmt, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
                             p.act == MOE_BF16, s) != hipSuccess)
       return MOE_ERR_HIP;
   }

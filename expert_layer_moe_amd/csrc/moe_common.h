@@ -46,6 +46,33 @@ __device__ __forceinline__ void store_y4(void* y, size_t idx, floatx4 v) {
     *reinterpret_cast<floatx4*>(static_cast<float*>(y) + idx) = v;
 }
 
+// y rows as 24-bit floats: the top three bytes of the fp32, rounded to
+// nearest even (bf16's range, 15 mantissa bits; NaN stays NaN).  Four
+// consecutive values take 12 bytes: a | b << 24, b >> 8 | c << 16,
+// c >> 16 | d << 8.
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+__device__ __forceinline__ uint32_t f32_to_f24_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 8) | 0x4000u;
+  return (u + 0x7fu + ((u >> 8) & 1u)) >> 8;
+}
+
+// four consecutive y values at element idx of a 24-bit y buffer
+__device__ __forceinline__ void store_y24(void* y, size_t idx, floatx4 v) {
+  const uint32_t a = f32_to_f24_bits(v[0]), b = f32_to_f24_bits(v[1]);
+  const uint32_t c = f32_to_f24_bits(v[2]), d = f32_to_f24_bits(v[3]);
+  *reinterpret_cast<u32x3*>(static_cast<uint8_t*>(y) + idx * 3) =
+      u32x3{a | (b << 24), (b >> 8) | (c << 16), (c >> 16) | (d << 8)};
+}
+
+__device__ __forceinline__ floatx4 unpack_y24(u32x3 w) {
+  return floatx4{__uint_as_float(w[0] << 8),
+                 __uint_as_float(((w[0] >> 24) | (w[1] << 8)) << 8),
+                 __uint_as_float(((w[1] >> 16) | (w[2] << 16)) << 8),
+                 __uint_as_float(w[2] & 0xffffff00u)};
+}
+
 // Eight consecutive values of y (a then b): fp32 (32 bytes) or bf16 (16).
 template <bool YB>
 __device__ __forceinline__ void store_y8(void* y, size_t idx, floatx4 a, floatx4 b) {

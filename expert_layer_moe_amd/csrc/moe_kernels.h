@@ -108,23 +108,25 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s);
 // y[r, :] = W2_e h[r, :] for every sorted row r (bf16 h in the layout
-// launch_gate_up writes; y rows fp32, bf16 with fp8 weights).  packed:
-// weights from launch_pack_weights.
+// launch_gate_up writes; y rows fp32, bf16 with fp8 weights, 24-bit floats
+// with bf16 weights when y24).  packed: weights from launch_pack_weights.
 hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
-                       int bm, int max_rows, hipStream_t s);
+                       int bm, int max_rows, bool y24, hipStream_t s);
 // Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
 // K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
 // s) of 512 elements at (t K/32 + s) 512, lane 16 g + m holding row 16 t + m,
 // columns 32 s + 8 g .. + 7.  `packed` kernels read this layout.
 hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t rows, int K,
                                hipStream_t s);
+// Formats of the expert output rows y.
+enum YFmt { Y_F32 = 0, Y_BF16 = 1, Y_F24 = 2 };
 // out[t] = sum_j w[t,j] y[pos(t,j)] (+ shared rows), summed in fp32 and
-// rounded once; y rows fp32, or bf16 when y_bf16.
-hipError_t launch_combine(const void* y, bool y_bf16, const int32_t* ids, const float* w,
+// rounded once; y rows in format yfmt.
+hipError_t launch_combine(const void* y, int yfmt, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
                           hipStream_t s);
