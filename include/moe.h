@@ -149,9 +149,11 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
 /* The whole layer: route -> align -> gate/up GEMM with SiLU(g)*u -> down GEMM
  * -> combine out[t] = sum_j w[t,j] * y_{ids[t,j]}(x_t) (+ shared experts with
  * weight 1), accumulated in fp32 and rounded once to act_dtype.  Each expert's
- * output row y is kept in fp32, or in bf16 when w_dtype is MOE_FP8_E4M3 (its
+ * output row y is kept in fp32; in bf16 when w_dtype is MOE_FP8_E4M3 (its
  * rounding, at most 2^-9 relative, sits well inside that path's error
- * budget).  `out` is fully overwritten; padding rows are set to 0.
+ * budget); with bf16 weights, in 24-bit floats (at most 2^-16 relative) when
+ * every expert segment of the call streams its weights.  `out` is fully
+ * overwritten; padding rows are set to 0.
  *   w13  [E+n_shared, 2I, H]: gate rows 0..I-1, then up rows I..2I-1
  *   w2   [E+n_shared, H, I]
  *   (fp8: uint8 e4m3fn codes; W = code value * block scale)
