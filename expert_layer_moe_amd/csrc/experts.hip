@@ -93,14 +93,22 @@ __device__ __forceinline__ int round_unit(int u0, int n_live) {
 // 233 / 254 on gather_padded_e48.)  Partial sums of the KS waves meet in LDS
 // (fixed order, one column tile at a time), then h = SiLU(g) * u in bf16.
 // Units: (item, column group), n_cg = ceil(I / (16 CGN 4 / KS)) per item.
-template <int KS, int MT, int KU, int CGN, bool FP8, bool PW>
+// XD: the token rows come straight from x (token sorted_ids[r] / topk of
+// sorted row r, row-major, 16 rows x 64 bytes per wave load) instead of the
+// fragment-ordered copy xp: for calls where every segment streams (decode)
+// x holds each token once where the copy holds it k times, and reading it
+// measured faster than packing it (decode_e48 step 0.265 -> 0.255 ms,
+// decode_e256_shared 0.500 -> 0.475 ms); with many rows per segment
+// (gather_padded_e48) the copy is faster (gate/up 241 against 288 us).
+template <int KS, int MT, int KU, int CGN, bool FP8, bool PW, bool XD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 || CGN > 1 ? 2 : 3)))
 void gate_up_stream_kernel(
     const uint16_t* __restrict__ xp, const void* __restrict__ w13,
     const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
-    uint16_t* __restrict__ h, int H, int I, int max_items, int n_cg) {
+    uint16_t* __restrict__ h, int H, int I, int max_items, int n_cg,
+    const int32_t* __restrict__ sorted_ids, int topk) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
   constexpr int CGW = 4 / KS;   // waves side by side along the columns
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
@@ -151,12 +159,22 @@ void gate_up_stream_kernel(
     // the item's 16-row tiles [tb, te) of the segment
     const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
     for (int t0 = tb; t0 < te; t0 += MT) {
-      // fragment-ordered token tiles (row0 is a multiple of 16); step s of
-      // tile t at xa + 512 s
+      // this lane's token row of each tile at the start of its K part:
+      // fragment-ordered tiles of xp (row0 is a multiple of 16; step s of
+      // tile t at xa + 512 s), or row m of the tile straight from x (XD;
+      // step s at xa + 32 s; a padding row reads any row: the MFMA keeps rows
+      // apart and its results are never stored)
       const uint16_t* xa[MT];
+      constexpr size_t xstep = XD ? 32 : 512;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
+      for (int mt = 0; mt < MT; ++mt) {
+        if constexpr (XD) {
+          const int sid = t0 + mt < te ? sorted_ids[row0 + (t0 + mt) * 16 + m] : -1;
+          xa[mt] = xp + (size_t)(sid >= 0 ? sid / topk : 0) * H + kbeg + 8 * g;
+        } else {
+          xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
+        }
+      }
       floatx4 ag[CGN][MT], au[CGN][MT];
 #pragma unroll
       for (int j = 0; j < CGN; ++j)
@@ -195,7 +213,7 @@ void gate_up_stream_kernel(
           for (int u = 0; u < KU; ++u)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * xstep) : zero);
           if constexpr (FP8) {
 #pragma unroll
             for (int j = 0; j < CGN; ++j) {
@@ -505,13 +523,20 @@ struct GuArgs {
   const int32_t* n_items;
   uint16_t* h;
   int H, I, max_items, n_cg;
+  const int32_t* sorted;   // with x_direct: the sorted row list, and
+  int topk;                // its entries per token row
+  bool x_direct;
 };
 
 template <int KS, int KU, bool FP8, bool PW>
 void launch_gu(const GuArgs& a) {
-  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, PW ? kGuCgn : 1, FP8, PW>), a.grid, dim3(256), 0, a.s,
-                     a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0,
-                     a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg);
+#define MOE_GU(XD)                                                                              \
+  hipLaunchKernelGGL((gate_up_stream_kernel<KS, 4, KU, PW ? kGuCgn : 1, FP8, PW, XD>), a.grid,   \
+                     dim3(256), 0, a.s, a.xp, a.w13, a.s13, a.seg_off, a.seg_cnt, a.item_seg,    \
+                     a.item_row0, a.n_items, a.h, a.H, a.I, a.max_items, a.n_cg, a.sorted, a.topk)
+  if (a.x_direct) MOE_GU(true);
+  else MOE_GU(false);
+#undef MOE_GU
 }
 
 // up to 4 K steps per batch, 2 with fp8 weights or without a K split (the
@@ -579,7 +604,7 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
                           const int32_t* seg_off, const int32_t* seg_cnt,
                           const int32_t* item_seg, const int32_t* item_row0,
                           const int32_t* n_items, int max_items, const void* xp, void* h,
-                          int H, int I, int k, int bm, int max_rows, hipStream_t s) {
+                          int H, int I, int k, int bm, int max_rows, bool x_direct, hipStream_t s) {
   if (wkind == W_F32) {
     hipLaunchKernelGGL(gate_up_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(w13),
@@ -596,9 +621,10 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
   const int cgw = 4 / ks * (packed ? kGuCgn : 1);   // 16-column tiles per block
   const int n_cg = (I / 16 + cgw - 1) / cgw;
   if (bm % 16 != 0 || (long long)max_items * n_cg > INT_MAX - 8) return hipErrorInvalidValue;
-  GuArgs a{dim3(stream_grid(max_items * n_cg)), s, static_cast<const uint16_t*>(xp), w13, s13,
-           seg_off, seg_cnt, item_seg, item_row0, n_items, static_cast<uint16_t*>(h), H, I,
-           max_items, n_cg};
+  GuArgs a{dim3(stream_grid(max_items * n_cg)), s,
+           static_cast<const uint16_t*>(x_direct ? x : xp), w13, s13, seg_off, seg_cnt, item_seg,
+           item_row0, n_items, static_cast<uint16_t*>(h), H, I, max_items, n_cg, sorted_ids, k,
+           x_direct};
   if (fp8) {
     if (packed) launch_gu_ks<true, true>(ks, ku, a);
     else launch_gu_ks<true, false>(ks, ku, a);

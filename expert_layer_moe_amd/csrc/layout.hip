@@ -22,34 +22,11 @@ namespace {
 // xp tile t = x rows of the sorted rows 16 t .. 16 t + 15.  Padding rows are
 // not written: an MFMA keeps the rows of its token operand apart, so whatever
 // they hold only reaches output rows that are never stored.
-// This kernel serves calls where every segment streams (no tiled GEMM):
-// grid = (cap / 16, chunks of kpc steps).
-__global__ __launch_bounds__(256) void pack_x_kernel(
-    const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ n_post, uint16_t* __restrict__ xp, int H, int k, int kpc) {
-  const int tile = blockIdx.x;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int m = lane % 16, g = lane / 16;
-  // issued together (the slot is inside the list's capacity; past n_post it
-  // holds a stale value that is never used): a short chain of dependent
-  // loads matters in a kernel this small
-  const int sid = sorted_ids[tile * 16 + m];
-  if (tile * 16 >= *n_post) return;
-  const uint16_t* src = x + (size_t)(sid >= 0 ? sid / k : 0) * H + 8 * g;
-  uint16_t* dst = xp + (size_t)tile * 16 * H + 8 * lane;
-  const int s0 = blockIdx.y * kpc, s1 = min(H / 32, s0 + kpc);
-  if (sid < 0) return;
-#pragma unroll 8
-  for (int s = s0 + wave; s < s1; s += 4)
-    *reinterpret_cast<u32x4*>(dst + (size_t)s * 512) = ld16(src + 32 * s);
-}
-
-// The same packing driven by the streaming kernels' item table, for calls
-// where the tiled GEMM may take the large segments: the work is then the
-// items of the few streaming segments, while a grid over every 16-row tile
-// of the sorted list spent the prefill micro-batch's 14 us mostly on blocks
-// that found their tile on the GEMM path.  Units (item, 16-row tile of the
-// item, chunk of kpc K steps), looped over by a capped grid.
+// Serves calls where the tiled GEMM may take the large segments (calls where
+// every segment streams read x directly): the work is the items of the
+// streaming segments, driven by the streaming kernels' item table.  Units
+// (item, 16-row tile of the item, chunk of kpc K steps), looped over by a
+// capped grid.
 __global__ __launch_bounds__(256) void pack_x_items_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
@@ -277,16 +254,6 @@ __global__ __launch_bounds__(256) void combine_ybf_kernel(
 }
 
 }  // namespace
-
-hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* n_post,
-                         void* xp, int H, int k, int max_rows, hipStream_t s) {
-  if (H % 32 != 0 || max_rows % 16 != 0) return hipErrorInvalidValue;
-  const int kpc = 32;   // MFMA steps per block
-  hipLaunchKernelGGL(pack_x_kernel, dim3(max_rows / 16, (H / 32 + kpc - 1) / kpc), dim3(256), 0,
-                     s, static_cast<const uint16_t*>(x), sorted_ids, n_post,
-                     static_cast<uint16_t*>(xp), H, k, kpc);
-  return hipGetLastError();
-}
 
 hipError_t launch_pack_x_items(const void* x, const int32_t* sorted_ids, const int32_t* seg_off,
                                const int32_t* seg_cnt, const int32_t* item_seg,

@@ -283,19 +283,20 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                           s) != hipSuccess)
       return MOE_ERR_HIP;
   }
-  if (wkind != moe::W_F32) {
+  // the streaming gate/up reads the token rows straight from x when every
+  // segment streams, else from a fragment-ordered copy of the streaming
+  // segments' rows
+  if (wkind != moe::W_F32 && gemm) {
     StageTimer tm(S_PACK_X, s);
-    const hipError_t e =
-        gemm ? moe::launch_pack_x_items(x, sorted, offs, cnt, iseg, irow, nitems, p.max_items, y,
-                                        p.H, p.k, s)
-             : moe::launch_pack_x(x, sorted, npost, y, p.H, p.k, p.cap, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (moe::launch_pack_x_items(x, sorted, offs, cnt, iseg, irow, nitems, p.max_items, y, p.H,
+                                 p.k, s) != hipSuccess)
+      return MOE_ERR_HIP;
   }
   {
     StageTimer tm(S_GATE_UP, s);
     if (moe::launch_gate_up(wkind, packed, x, w13, desc->w13_scale, sorted, bexp, npost, offs,
                             cnt, iseg, irow, nitems, p.max_items, y, h, p.H, p.I, p.k, p.bm,
-                            p.cap, s) != hipSuccess)
+                            p.cap, !gemm, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
   uint8_t* xq = p.xsplit ? at<uint8_t>(ws, p.off_xq) : nullptr;

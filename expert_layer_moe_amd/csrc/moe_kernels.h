@@ -58,13 +58,10 @@ inline int max_stream_items(long long n_rows, int nseg) {
 // their per-block table of 128-wide scale blocks).
 constexpr int kMaxGemmK = 16384;
 
-// bf16 streaming path, calls without the tiled GEMM: x rows of the sorted
-// rows (the first *n_post of max_rows), packed in MFMA fragment order into xp
-// (max_rows x H bf16, 16-row tiles; padding rows left as they are).
-hipError_t launch_pack_x(const void* x, const int32_t* sorted_ids, const int32_t* n_post,
-                         void* xp, int H, int k, int max_rows, hipStream_t s);
-// The same packing for calls where the tiled GEMM may run: only the rows of
-// the stream item table's items (the streaming segments) are packed.
+// bf16 streaming path, calls where the tiled GEMM may run: x rows of the
+// sorted rows of the stream item table's items (the streaming segments),
+// packed in MFMA fragment order into xp (sorted-list rows x H bf16, 16-row
+// tiles; padding rows and rows of other segments left as they are).
 hipError_t launch_pack_x_items(const void* x, const int32_t* sorted_ids, const int32_t* seg_off,
                                const int32_t* seg_cnt, const int32_t* item_seg,
                                const int32_t* item_row0, const int32_t* n_items, int max_items,
@@ -73,16 +70,19 @@ hipError_t launch_pack_x_items(const void* x, const int32_t* sorted_ids, const i
 // the stream item table (item_seg, item_row0: a segment and the first of up
 // to 64 of its rows; *n_items of them, at most max_items; segments at
 // seg_off[e] .. + seg_cnt[e] of the sorted list).
-// bf16: the token rows come from xp (launch_pack_x), and h rows of the
-// streaming kernels' segments are written in fragment order too (16-row
-// tiles; the GEMM kernels' rows stay row-major).  fp32 reads x directly.
+// bf16 / fp8 weights: the token rows come from xp (launch_pack_x_items), or
+// straight from x (bf16 [T, H]) through sorted_ids when x_direct (calls where
+// every segment streams); h rows of the streaming kernels' segments are
+// written in fragment order (16-row tiles; the GEMM kernels' rows stay
+// row-major).  fp32 reads x directly.
 hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13,
                           const float* s13, const int32_t* sorted_ids,
                           const int32_t* block_expert, const int32_t* n_post,
                           const int32_t* seg_off, const int32_t* seg_cnt,
                           const int32_t* item_seg, const int32_t* item_row0,
                           const int32_t* n_items, int max_items, const void* xp, void* h,
-                          int H, int I, int k, int bm, int max_rows, hipStream_t s);
+                          int H, int I, int k, int bm, int max_rows, bool x_direct,
+                          hipStream_t s);
 // Tiled GEMMs for segments with more than big_thr rows (the align's tile
 // table), and the router GEMM for large batches.  K (H, I) % 128 == 0.
 // fp8 weights with xq non-null: the fp8-MFMA kernel on the two-term token
