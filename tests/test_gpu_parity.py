@@ -505,6 +505,55 @@ def test_gather_nan_padding_rows_are_never_read():
     assert np.array_equal(a["ids"], b["ids"])
 
 
+@pytest.mark.parametrize("kw", [
+    dict(T=1500, H=256, E=13, k=3, I=64, valid_frac=0.3),            # tiled router
+    dict(T=1030, H=384, E=100, k=5, I=128, n_shared=1, valid_frac=0.5),
+    dict(T=1200, H=256, E=64, k=8, I=128, w="fp8", valid_frac=0.2),   # bf16 y rows
+    dict(T=1100, H=256, E=200, k=4, I=64, valid_frac=0.4),           # the 256-expert router GEMM
+    dict(T=300, H=256, E=8, k=2, I=64, valid_frac=0.5),              # small batch router
+])
+def test_padding_output_rows_are_zeroed_whatever_out_held(kw):
+    """Every output row of a padding token is written with zeros (out filled
+    with NaN beforehand), for each router and combine variant."""
+    inp = random_small(seed=77, **kw)
+    log(f"[case] padding rows zeroed in a NaN-filled out: {kw}")
+    layer = device_layer(inp, packed=True)
+    xd, vd = inp.x.cuda(), inp.valid.cuda()
+    out = torch.full_like(xd, float("nan"))
+    layer.forward(xd, vd, out=out)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    pad = inp.valid == 0
+    assert pad.any() and (o[pad] == 0).all()
+    assert torch.isfinite(o).all()
+    ref = run_gpu(inp, layer)["out"]
+    assert np.array_equal(o.double().numpy(), ref)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("ns", [0, 1])
+def test_all_streaming_nan_padding_rows_are_never_read(packed, ns):
+    """A layer whose segments all stream (its gate/up reads the token rows
+    straight from x through the sorted list, padding slots of the list
+    pointing at row 0) with row 0 and every other padding row NaN: the same
+    output bits as with finite padding rows, zero rows for padding tokens,
+    and the oracle's result."""
+    inp = random_small(T=200, H=512, E=8, k=2, I=128, n_shared=ns, valid_frac=0.6,
+                       seed=321 + ns)
+    inp.valid[0] = 0
+    log(f"[case] all-streaming layer with NaN padding rows, packed={packed} ns={ns}")
+    layer = device_layer(inp, packed=packed)
+    a = run_gpu(inp, layer)
+    x_nan = inp.x.clone()
+    x_nan[inp.valid == 0] = float("nan")
+    b = run_gpu(inp, layer, x=x_nan)
+    assert np.array_equal(a["out"], b["out"])
+    assert np.array_equal(a["ids"], b["ids"])
+    assert np.isfinite(b["out"]).all()
+    assert (b["out"][inp.valid.numpy() == 0] == 0).all()
+    compare(inp, a)
+
+
 def test_prefill_two_streams_match_unsplit_batch():
     """ub0 and ub1 (midpoint split) on two HIP streams give exactly the rows of
     the unsplit 16384-row batch; ub1 also matches the oracle."""
