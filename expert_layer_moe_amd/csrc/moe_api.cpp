@@ -172,8 +172,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   // every segment streams (only the streaming down kernel writes them), fp32
   // otherwise.  The room is that of fp32 rows with bf16 weights whatever the
   // format, so that the workspace size does not depend on the path
-  // thresholds.  It also holds the packed token rows of the streaming
-  // gate/up (cap x H bf16) until the down kernels overwrite them.
+  // thresholds.  In calls where the tiled GEMM may run it also holds the
+  // packed token rows of the streaming gate/up (cap x H bf16) until the down
+  // kernels overwrite them.
   p->yfmt = p->w == MOE_FP8_E4M3 ? moe::Y_BF16
             : (p->w == MOE_BF16 && p->big_thr == INT_MAX) ? moe::Y_F24 : moe::Y_F32;
   p->off_y = take((size_t)p->cap * p->H * (p->w == MOE_FP8_E4M3 ? 2 : 4));
