@@ -45,6 +45,27 @@ def _d(**kw):
     return moe_desc(**base)
 
 
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A C99 program (tests/c_abi/abi_smoke.c) includes moe.h with strict
+    warnings as errors, links libmoe_amd.so and calls the host-side entry
+    points (nothing is launched)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lib = LIB_PATH
+    src = os.path.join(os.path.dirname(__file__), "c_abi", "abi_smoke.c")
+    exe = str(tmp_path / "abi_smoke")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-I", os.path.dirname(HEADER), src, "-o", exe, lib,
+                        "-Wl,-rpath," + os.path.dirname(lib)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "abi smoke: ok" in r.stdout, r.stdout + r.stderr
+
+
 def test_status_strings():
     for s in (0, -1, -2, -3, -4):
         assert moe.moe_status_str(s)
