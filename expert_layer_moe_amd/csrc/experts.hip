@@ -452,6 +452,148 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   }
 }
 
+// Down projection and combine in one launch, for calls where every segment
+// streams and the batch holds at most kColsRows assignments (decode): one
+// block per 32 output columns runs every segment's rows against its W2
+// columns, keeps each assignment's output row (those 32 columns, fp32) in
+// LDS, then forms out[t] = sum_j w[t,j] y(t,j) for those columns itself.
+// No y rows go to memory and back, and no combine launch follows.  The
+// block's 16 waves take the segments in turn; a wave streams its segment's
+// two 16-column W2 tiles over K = I (the MFMA A operand) for up to MT = 2
+// of the segment's 16-row h tiles at a time.  The sums run over K in the
+// order of the streaming down kernel, and the combine in the order of the
+// combine kernels (slot j = 0, 1, ...; the shared slot with weight 1).
+constexpr int kColsRows = 1024;   // LDS rows: assignments (T (k + n_shared))
+
+template <int KU, bool FP8, bool PW>
+__global__ __launch_bounds__(1024) void down_cols_kernel(
+    const uint16_t* __restrict__ h, const void* __restrict__ w2, const float* __restrict__ s2,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ ids,
+    const float* __restrict__ wts, int T, int H, int I, int E, int ns, int k,
+    uint16_t* __restrict__ out) {
+  constexpr int NT = 2, MT = 2, NW = 16;
+  // y(a)[32 columns] of assignment a = t (k + ns) + j, as 8 groups of 4
+  __shared__ floatx4 ylds[kColsRows][NT * 4];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int m = lane % 16, g = lane / 16;
+  const int c0 = blockIdx.x * NT * 16;
+  const int nseg = E + ns, kk = k + ns;
+  constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int seg = wave; seg < nseg; seg += NW) {
+    const int cnt = seg_cnt[seg];
+    if (cnt == 0) continue;
+    const int row0 = seg_off[seg];
+    size_t wo[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // a tile past H (H % 32 == 16) re-reads the last one; never combined
+      const int n = min(c0 + nt * 16, H - 16);
+      if constexpr (PW) wo[nt] = (((size_t)seg * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
+      else wo[nt] = ((size_t)seg * H + n + m) * I + 8 * g;
+    }
+    const float* sc = nullptr;
+    if constexpr (FP8) sc = s2 + (size_t)seg * (H / 128) * (I / 128);
+    const int ntl = (cnt + 15) >> 4;
+    for (int t0 = 0; t0 < ntl; t0 += MT) {
+      const uint16_t* ha[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
+      floatx4 acc[MT][NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // W2 columns read once by this block (a segment in one pass):
+      // non-temporal loads
+      auto k_loop = [&](auto nt_tag) {
+        constexpr bool kNT = decltype(nt_tag)::value;
+        for (int k0 = 0; k0 < I; k0 += 32 * KU) {
+          bf16x8 b[KU][NT], a[KU][MT];
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(k0 / 32 + u) * wstep);
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              a[u][mt] = as_bf16x8(t0 + mt < ntl ? ld16(ha[mt] + (size_t)(k0 / 32 + u) * 512) : zero);
+          if constexpr (FP8) {
+            floatx4 p[MT][NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < ntl)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
+            const int kb = k0 >> 7;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const float sv = sc[((size_t)min(c0 + nt * 16, H - 16) / 128) * (I / 128) + kb];
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(sv, p[mt][nt][i], acc[mt][nt][i]);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < ntl)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
+          }
+        }
+      };
+      if (PW && ntl <= MT) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
+      // acc[mt][nt] lane (m, g): columns c0 + 16 nt + 4 g .. + 3 of the
+      // segment's row (t0 + mt) 16 + m, whose list entry is t k + j (t k for
+      // the shared segment E)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = (t0 + mt) * 16 + m;
+        if (t0 + mt >= ntl || r >= cnt) continue;
+        const int entry = sorted_ids[row0 + r];
+        const int tt = entry / k;
+        const int a = seg < E ? entry + tt * ns : tt * kk + k;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ylds[a][4 * nt + g] = acc[mt][nt];
+      }
+    }
+  }
+  __syncthreads();
+  // out[t] for this block's columns: thread -> (token, group of 4 columns)
+  for (int i = threadIdx.x; i < T * NT * 4; i += blockDim.x) {
+    const int t = i / (NT * 4), q = i - t * (NT * 4);
+    const int col = c0 + 4 * q;
+    if (col >= H) continue;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (ids[(size_t)t * k] >= 0) {
+      for (int j = 0; j < kk; ++j) {
+        const float wt = j < k ? wts[(size_t)t * k + j] : 1.f;
+        const floatx4 v = ylds[t * kk + j][q];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = fmaf(wt, v[c], acc[c]);
+      }
+    }
+    u32x2 pk;
+    pk[0] = pack_bf16x2(acc[0], acc[1]);
+    pk[1] = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<u32x2*>(out + (size_t)t * H + col) = pk;
+  }
+}
+
 // fp32 layers (small): one block per sorted row, plain FMA loops.
 __global__ __launch_bounds__(256) void gate_up_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ w13,
@@ -632,6 +774,37 @@ hipError_t launch_gate_up(int wkind, bool packed, const void* x, const void* w13
     if (packed) launch_gu_ks<false, true>(ks, ku, a);
     else launch_gu_ks<false, false>(ks, ku, a);
   }
+  return hipGetLastError();
+}
+
+bool down_cols_fits(int T, int k, int n_shared, int H, int I) {
+  return (long long)T * (k + n_shared) <= kColsRows && H % 16 == 0 && I % 32 == 0;
+}
+
+hipError_t launch_down_cols(int wkind, bool packed, const void* h, const void* w2,
+                            const float* s2, const int32_t* seg_off, const int32_t* seg_cnt,
+                            const int32_t* sorted_ids, const int32_t* ids, const float* w,
+                            int T, int H, int I, int E, int n_shared, int k, void* out,
+                            hipStream_t s) {
+  if (wkind == W_F32 || !down_cols_fits(T, k, n_shared, H, I)) return hipErrorInvalidValue;
+  const bool fp8 = wkind == W_FP8;
+  const int ku = pick_ku(I);
+  const dim3 grid((H + 31) / 32);
+#define MOE_DC(KU, F, P)                                                                       \
+  hipLaunchKernelGGL((down_cols_kernel<KU, F, P>), grid, dim3(1024), 0, s,                      \
+                     static_cast<const uint16_t*>(h), w2, s2, seg_off, seg_cnt, sorted_ids, ids, \
+                     w, T, H, I, E, n_shared, k, static_cast<uint16_t*>(out))
+#define MOE_DC_KU(F, P)            \
+  if (ku == 4) MOE_DC(4, F, P);    \
+  else if (ku == 2) MOE_DC(2, F, P); \
+  else MOE_DC(1, F, P)
+  if (fp8) {
+    if (packed) { MOE_DC_KU(true, true); } else { MOE_DC_KU(true, false); }
+  } else {
+    if (packed) { MOE_DC_KU(false, true); } else { MOE_DC_KU(false, false); }
+  }
+#undef MOE_DC_KU
+#undef MOE_DC
   return hipGetLastError();
 }
 

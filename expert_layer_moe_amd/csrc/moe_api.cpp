@@ -34,6 +34,7 @@ struct Plan {
       off_span, off_h, off_y, off_xq, off_sx, total;
   bool xsplit;    // fp8 weights on the GEMM path: token rows as two e4m3 terms
   int yfmt;       // format of the expert output rows y (moe::YFmt)
+  bool down_cols; // down projection and combine in one launch (small batches)
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -178,6 +179,10 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->yfmt = p->w == MOE_FP8_E4M3 ? moe::Y_BF16
             : (p->w == MOE_BF16 && p->big_thr == INT_MAX) ? moe::Y_F24 : moe::Y_F32;
   p->off_y = take((size_t)p->cap * p->H * (p->w == MOE_FP8_E4M3 ? 2 : 4));
+  // every segment streams and the batch's assignments fit the combined
+  // down kernel's LDS rows: no y rows, no combine launch
+  p->down_cols = p->big_thr == INT_MAX && p->w != MOE_F32 && p->act == MOE_BF16 &&
+                 moe::down_cols_fits(p->T, p->k, p->ns, p->H, p->I);
   // two e4m3 code planes of the token rows and their scales (fp8 MFMA path):
   // room whenever the shape can take the tiled GEMM (so the workspace size
   // does not depend on the path thresholds); filled when it can run
@@ -312,6 +317,14 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                                  trow, ntiles, offs, cnt, h, p.H, p.I, p.k, p.max_tiles, xq, sx,
                                  p.T, s) != hipSuccess)
       return MOE_ERR_HIP;
+  }
+  if (p.down_cols) {
+    // the down projection and the combine in one launch
+    StageTimer tm(S_DOWN, s);
+    if (moe::launch_down_cols(wkind, packed, h, w2, desc->w2_scale, offs, cnt, sorted, ids, wts,
+                              p.T, p.H, p.I, p.E, p.ns, p.k, out, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
   }
   {
     StageTimer tm(S_DOWN, s);

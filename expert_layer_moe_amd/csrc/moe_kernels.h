@@ -107,6 +107,15 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
 // with no valid row are skipped (their partials are never read).
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s);
+// Calls where every segment streams, bf16 / fp8 weights, at most 1024
+// assignments (T (k + n_shared)): the down projection and the combine in one
+// launch, out [T, H] bf16 written directly (padding rows zero).
+bool down_cols_fits(int T, int k, int n_shared, int H, int I);
+hipError_t launch_down_cols(int wkind, bool packed, const void* h, const void* w2,
+                            const float* s2, const int32_t* seg_off, const int32_t* seg_cnt,
+                            const int32_t* sorted_ids, const int32_t* ids, const float* w,
+                            int T, int H, int I, int E, int n_shared, int k, void* out,
+                            hipStream_t s);
 // y[r, :] = W2_e h[r, :] for every sorted row r (bf16 h in the layout
 // launch_gate_up writes; y rows fp32, bf16 with fp8 weights, 24-bit floats
 // with bf16 weights when y24).  packed: weights from launch_pack_weights.
