@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 // of the segment's 16-row h tiles at a time.  The sums run over K in the
 // order of the streaming down kernel, and the combine in the order of the
 // combine kernels (slot j = 0, 1, ...; the shared slot with weight 1).
-constexpr int kColsRows = 1024;   // LDS rows: assignments (T (k + n_shared))
+constexpr int kColsRows = 1216;   // LDS rows: assignments (T (k + n_shared)); 152 KB
 
 template <int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(1024) void down_cols_kernel(

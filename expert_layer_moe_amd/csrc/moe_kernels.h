@@ -107,7 +107,7 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
 // with no valid row are skipped (their partials are never read).
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
                               float* part, int T, int H, int E, int ks, hipStream_t s);
-// Calls where every segment streams, bf16 / fp8 weights, at most 1024
+// Calls where every segment streams, bf16 / fp8 weights, at most 1216
 // assignments (T (k + n_shared)): the down projection and the combine in one
 // launch, out [T, H] bf16 written directly (padding rows zero).
 bool down_cols_fits(int T, int k, int n_shared, int H, int I);

@@ -530,6 +530,22 @@ def test_padding_output_rows_are_zeroed_whatever_out_held(kw):
     assert np.array_equal(o.double().numpy(), ref)
 
 
+@pytest.mark.parametrize("kw", [
+    dict(T=152, H=512, E=64, k=8, I=128),                      # 1216 assignments: one launch
+    dict(T=153, H=512, E=64, k=8, I=128),                      # 1224: down, then combine
+    dict(T=135, H=384, E=100, k=8, I=64, n_shared=1, valid_frac=0.9),   # 1215 with the shared slot
+    dict(T=152, H=256, E=64, k=8, I=128, w="fp8", valid_frac=0.7),
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_down_and_combine_in_one_launch_at_its_row_limit(kw, packed):
+    """Small batches where every segment streams run the down projection and
+    the combine in one launch while their assignments fit its 1216 LDS rows,
+    and in two launches past that; both match the oracle."""
+    inp = random_small(seed=1216 + kw["T"], **kw)
+    log(f"[case] down + combine row limit, packed={packed}: {kw}")
+    compare(inp, run_gpu(inp, device_layer(inp, packed=packed)))
+
+
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("ns", [0, 1])
 def test_all_streaming_nan_padding_rows_are_never_read(packed, ns):
