@@ -152,8 +152,10 @@ int moe_align(const moe_desc* desc, const int32_t* topk_ids, int32_t topk,
  * output row y is kept in fp32; in bf16 when w_dtype is MOE_FP8_E4M3 (its
  * rounding, at most 2^-9 relative, sits well inside that path's error
  * budget); with bf16 weights, in 24-bit floats (at most 2^-16 relative) when
- * every expert segment of the call streams its weights.  `out` is fully
- * overwritten; padding rows are set to 0.
+ * every expert segment of the call streams its weights.  Calls where every
+ * segment streams and T*(topk+n_shared) <= 1216 keep the y rows in fp32 on
+ * chip and combine them in the same launch, whatever w_dtype.  `out` is
+ * fully overwritten; padding rows are set to 0.
  *   w13  [E+n_shared, 2I, H]: gate rows 0..I-1, then up rows I..2I-1
  *   w2   [E+n_shared, H, I]
  *   (fp8: uint8 e4m3fn codes; W = code value * block scale)
