@@ -464,6 +464,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 // order of the streaming down kernel, and the combine in the order of the
 // combine kernels (slot j = 0, 1, ...; the shared slot with weight 1).
 constexpr int kColsRows = 1216;   // LDS rows: assignments (T (k + n_shared)); 152 KB
+constexpr int kMaxSegments = 257;  // 256 routed experts + 1 shared
 
 template <int KU, bool FP8, bool PW>
 __global__ __launch_bounds__(1024) void down_cols_kernel(
@@ -475,16 +476,24 @@ __global__ __launch_bounds__(1024) void down_cols_kernel(
   constexpr int NT = 2, MT = 2, NW = 16;
   // y(a)[32 columns] of assignment a = t (k + ns) + j, as 8 groups of 4
   __shared__ floatx4 ylds[kColsRows][NT * 4];
+  // every segment's offset and row count, read once per block (the waves
+  // would otherwise wait for them at each segment they start)
+  __shared__ int s_off[kMaxSegments], s_cnt[kMaxSegments];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int m = lane % 16, g = lane / 16;
   const int c0 = blockIdx.x * NT * 16;
   const int nseg = E + ns, kk = k + ns;
   constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < nseg; i += blockDim.x) {
+    s_off[i] = seg_off[i];
+    s_cnt[i] = seg_cnt[i];
+  }
+  __syncthreads();
   for (int seg = wave; seg < nseg; seg += NW) {
-    const int cnt = seg_cnt[seg];
+    const int cnt = s_cnt[seg];
     if (cnt == 0) continue;
-    const int row0 = seg_off[seg];
+    const int row0 = s_off[seg];
     size_t wo[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -498,9 +507,14 @@ __global__ __launch_bounds__(1024) void down_cols_kernel(
     const int ntl = (cnt + 15) >> 4;
     for (int t0 = 0; t0 < ntl; t0 += MT) {
       const uint16_t* ha[MT];
+      // list entries of this pass's rows, loaded ahead of the K loop
+      int entry[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt) {
         ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
+        const int r = (t0 + mt) * 16 + m;
+        entry[mt] = r < cnt ? sorted_ids[row0 + r] : 0;
+      }
       floatx4 acc[MT][NT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -564,9 +578,8 @@ __global__ __launch_bounds__(1024) void down_cols_kernel(
       for (int mt = 0; mt < MT; ++mt) {
         const int r = (t0 + mt) * 16 + m;
         if (t0 + mt >= ntl || r >= cnt) continue;
-        const int entry = sorted_ids[row0 + r];
-        const int tt = entry / k;
-        const int a = seg < E ? entry + tt * ns : tt * kk + k;
+        const int tt = entry[mt] / k;
+        const int a = seg < E ? entry[mt] + tt * ns : tt * kk + k;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) ylds[a][4 * nt + g] = acc[mt][nt];
       }
