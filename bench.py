@@ -12,12 +12,16 @@ every other workload with its own step count and nests the results under
 mixed-phase gather, the 8192-row prefill micro-batch with fp8 weights (the
 MFMA-bound half of the metric), the two micro-batches on two HIP streams,
 the unsplit 16384-row batch and the request-boundary split (7003 / 9381),
-and the tiny fp32 correctness layer.  Prints one JSON line.
+the tiny fp32 correctness layer, and the gather and the prefill micro-batch
+through moe_forward_signaled (per-(expert, 64-row block) completion counters
+from the down kernels, the combine consuming them on a second stream).
+Prints one JSON line.
 
 Other modes (profiling runs; the default run takes none of them):
   --config NAME       only that workload (tiny, decode_e48, decode_e256_shared,
                       gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8,
-                      prefill_unsplit, prefill_boundary_split)
+                      prefill_unsplit, prefill_boundary_split,
+                      gather_padded_e48_signaled, prefill_ub_fp8_signaled)
   --no-cpu-baseline   skip the oracle timing
   --copy-calibrate    time a plain 1 GiB device copy (for counter scaling)
 """
@@ -44,7 +48,12 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # the headline workload, and the others measured in the same run
 HEADLINE = "decode_e48"
 NESTED = ["decode_e256_shared", "gather_padded_e48", "prefill_ub_fp8", "prefill_pair_fp8",
-          "prefill_unsplit", "prefill_boundary_split", "tiny"]
+          "prefill_unsplit", "prefill_boundary_split", "tiny",
+          "gather_padded_e48_signaled", "prefill_ub_fp8_signaled"]
+# workloads run through moe_forward_signaled: the down kernels raise
+# per-(expert, 64-row block) completion counters and the combine consumes
+# them on a second stream
+SIGNALED = "_signaled"
 # two-call variants of the prefill workload: (first rows, second rows)
 PREFILL_SPLITS = {"prefill_pair_fp8": "midpoint", "prefill_boundary_split": "boundary"}
 
@@ -204,9 +213,11 @@ class Workload:
         from workloads.configs import boundary_split, midpoint_split
 
         self.name = name
-        self.split = PREFILL_SPLITS.get(name)
-        whole = name in ("prefill_unsplit",) or self.split is not None
-        base = get_config("prefill_ub_fp8" if whole else name)
+        self.signaled = name.endswith(SIGNALED)
+        bname = name[:-len(SIGNALED)] if self.signaled else name
+        self.split = PREFILL_SPLITS.get(bname)
+        whole = bname in ("prefill_unsplit",) or self.split is not None
+        base = get_config("prefill_ub_fp8" if whole else bname)
         self.cfg = base.with_(T=base.full_T, ub=None) if whole else base
         log(f"[bench] generating {name}")
         self.inp = make_inputs(self.cfg)
@@ -221,6 +232,9 @@ class Workload:
         if self.split is None:
             self.parts = None
             self.ws = self.layer.workspace(c.T)
+            if self.signaled:
+                self.sig = self.layer.block_signals(c.T)
+                self.consumer = torch.cuda.Stream()
         else:
             a, b = (midpoint_split(c.T) if self.split == "midpoint"
                     else boundary_split(list(base.requests)))
@@ -237,7 +251,11 @@ class Workload:
     def step(self):
         import torch
         if self.parts is None:
-            self.layer.forward(self.x, self.valid, self.out, self.ws)
+            if self.signaled:
+                self.layer.forward_signaled(self.x, self.valid, self.out, self.ws, self.sig,
+                                            consumer_stream=self.consumer)
+            else:
+                self.layer.forward(self.x, self.valid, self.out, self.ws)
             return
         cur = torch.cuda.current_stream()
         ev = torch.cuda.Event()
@@ -306,6 +324,8 @@ def config_of(wl):
            "topk": c.k, "I": c.I, "n_shared": c.n_shared, "weights": c.w,
            "weight_layout": "frag16" if wl.packed else "row_major",
            "two_streams": wl.parts is not None}
+    if wl.signaled:
+        cfg["block_signals"] = True
     if wl.parts is not None:
         cfg["calls_rows"] = list(wl.rows)
     return cfg

@@ -22,7 +22,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
-           "moe_forward_noalloc",
+           "moe_forward_noalloc", "moe_forward_signaled", "moe_block_signal_count", "moe_set_signal_wait_us",
            "moe_pack_weights", "moe_set_path_thresholds", "moe_set_fp8_mfma", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
@@ -65,6 +65,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward_noalloc.argtypes = [D, P, P, P, P, P, I32, P, P]
     lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_signaled.argtypes = [D, P, P, P, P, P, I32, P, P, SZ, P, P, P]
+    lib.moe_forward_signaled.restype = ctypes.c_int
+    lib.moe_block_signal_count.argtypes = [D]
+    lib.moe_block_signal_count.restype = SZ
+    lib.moe_set_signal_wait_us.argtypes = [I32]
+    lib.moe_set_signal_wait_us.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.moe_set_fp8_mfma.argtypes = [I32]
@@ -204,6 +210,34 @@ def moe_forward_noalloc(desc, x, valid_rows, router_w, w13, w2, topk, out, strea
         _dev(w13, "w13", _w(desc), (E + ns, 2 * I, H)),
         _dev(w2, "w2", _w(desc), (E + ns, H, I)), topk,
         _dev(out, "out", _act(desc), (T, H)), _stream(stream)))
+
+
+def moe_block_signal_count(desc: moe_desc) -> int:
+    """Entries of moe_forward_signaled's completion counters."""
+    return int(load_library().moe_block_signal_count(ctypes.byref(desc)))
+
+
+def moe_forward_signaled(desc, x, valid_rows, router_w, w13, w2, topk, out, workspace,
+                         block_signal, stream=None, consumer_stream=None):
+    """moe_forward with per-(expert, 64-row block) completion counters
+    (block_signal, int32 [E + n_shared, ceil(T / 64)]) and the combine waiting
+    on them on consumer_stream (None: the current stream, like `stream`)."""
+    T, H, E, I, ns = desc.T, desc.H, desc.E, desc.I, desc.n_shared
+    _check(load_library().moe_forward_signaled(
+        ctypes.byref(desc), _dev(x, "x", _act(desc), (T, H)),
+        _dev(valid_rows, "valid_rows", torch.uint8, (T,)),
+        _dev(router_w, "router_w", _act(desc), (E, H)),
+        _dev(w13, "w13", _w(desc), (E + ns, 2 * I, H)),
+        _dev(w2, "w2", _w(desc), (E + ns, H, I)), topk,
+        _dev(out, "out", _act(desc), (T, H)),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _dev(block_signal, "block_signal", torch.int32, (E + ns, (T + 63) // 64)),
+        _stream(stream), _stream(consumer_stream)))
+
+
+def moe_set_signal_wait_us(us: int = 10000):
+    """Time bound of each wait of the signaled combine (process-wide)."""
+    _check(load_library().moe_set_signal_wait_us(us))
 
 
 SCRATCH_BYTES = 64 << 20   # MOE_SCRATCH_BYTES

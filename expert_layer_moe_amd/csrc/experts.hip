@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
-    void* __restrict__ y, int H, int I, int max_items, int n_ng) {
+    void* __restrict__ y, int H, int I, int max_items, int n_ng, BlockSignals bs) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
   static_assert(NT == 4, "the store pass moves 64-column tiles");
   // per wave: one 16-row x 64-column tile of y on its way out (rows padded
@@ -345,110 +345,117 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
     const int row0 = seg_off[e];
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
     const int n0 = (ngb * 4 + wave) * NT * 16;
-    if (n0 >= H) continue;   // no barriers here: waves go their own way
-    const int m = lane % 16, g = lane / 16;
-    constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
-    size_t wo[NT];
+    // no barriers in a unit (waves go their own way) unless it raises a
+    // completion signal at its end
+    if (n0 < H) {
+      const int m = lane % 16, g = lane / 16;
+      constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
+      size_t wo[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = min(n0 + nt * 16, H - 16);
-      if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
-      else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
-    }
-    const float* sc = nullptr;
-    if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    // the item's 16-row tiles [tb, te) of the segment
-    const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
-    for (int t0 = tb; t0 < te; t0 += MT) {
-      // fragment-ordered h tiles (rows past cnt may hold anything: each token
-      // row feeds only its own output column of the MFMA, never stored)
-      const uint16_t* ha[MT];
+      for (int nt = 0; nt < NT; ++nt) {
+        const int n = min(n0 + nt * 16, H - 16);
+        if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
+        else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
+      }
+      const float* sc = nullptr;
+      if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      // the item's 16-row tiles [tb, te) of the segment
+      const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
+      for (int t0 = tb; t0 < te; t0 += MT) {
+        // fragment-ordered h tiles (rows past cnt may hold anything: each token
+        // row feeds only its own output column of the MFMA, never stored)
+        const uint16_t* ha[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
-      floatx4 acc[MT][NT];
+        for (int mt = 0; mt < MT; ++mt)
+          ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
+        floatx4 acc[MT][NT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      // W2 of a segment with one item is read by this block alone: non-temporal
-      // loads (measured faster); the items of a larger segment share it
-      // through L2 (normal loads measured faster)
-      auto k_loop = [&](auto nt_tag) {
-        constexpr bool kNT = decltype(nt_tag)::value;
-        for (int kk = 0; kk < I; kk += 32 * KU) {
-          bf16x8 b[KU][NT], a[KU][MT];
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // W2 of a segment with one item is read by this block alone: non-temporal
+        // loads (measured faster); the items of a larger segment share it
+        // through L2 (normal loads measured faster)
+        auto k_loop = [&](auto nt_tag) {
+          constexpr bool kNT = decltype(nt_tag)::value;
+          for (int kk = 0; kk < I; kk += 32 * KU) {
+            bf16x8 b[KU][NT], a[KU][MT];
 #pragma unroll
-          for (int u = 0; u < KU; ++u)
+            for (int u = 0; u < KU; ++u)
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-              b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
-          if constexpr (FP8) {
-            floatx4 p[MT][NT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+              for (int nt = 0; nt < NT; ++nt)
+                b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
 #pragma unroll
             for (int u = 0; u < KU; ++u)
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
-                if (t0 + mt < te)
-#pragma unroll
-                  for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
-            const int kb = kk >> 7;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-              const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+                a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+            if constexpr (FP8) {
+              floatx4 p[MT][NT];
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+                for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int u = 0; u < KU; ++u)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  if (t0 + mt < te)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
+              const int kb = kk >> 7;
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) {
+                const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                  for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+              }
+            } else {
+#pragma unroll
+              for (int u = 0; u < KU; ++u)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  if (t0 + mt < te)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
             }
-          } else {
-#pragma unroll
-            for (int u = 0; u < KU; ++u)
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                if (t0 + mt < te)
-#pragma unroll
-                  for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
           }
-        }
-      };
-      // (fragment-packed weights only: a row-major K step reads half of each
-      // 128-byte line, and the next step needs the line again)
-      if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
-      else k_loop(std::false_type{});
-      // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt +
-      // 4 g .. + 3.  Through LDS: lane l then holds row 4 q + l / 16 of the
-      // tile, columns n0 + 4 (l % 16) .. + 3, for q = 0 .. 3.
-      const int lr = lane / 16, lc = lane % 16;
-      const bool col_in = n0 + 4 * lc < H;   // H is a multiple of 16
+        };
+        // (fragment-packed weights only: a row-major K step reads half of each
+        // 128-byte line, and the next step needs the line again)
+        if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
+        else k_loop(std::false_type{});
+        // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt +
+        // 4 g .. + 3.  Through LDS: lane l then holds row 4 q + l / 16 of the
+        // tile, columns n0 + 4 (l % 16) .. + 3, for q = 0 .. 3.
+        const int lr = lane / 16, lc = lane % 16;
+        const bool col_in = n0 + 4 * lc < H;   // H is a multiple of 16
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if (t0 + mt >= te) continue;
+        for (int mt = 0; mt < MT; ++mt) {
+          if (t0 + mt >= te) continue;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) ytile[wave][m][4 * nt + g] = acc[mt][nt];
+          for (int nt = 0; nt < NT; ++nt) ytile[wave][m][4 * nt + g] = acc[mt][nt];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tr = 4 * q + lr;
-          const int r = (t0 + mt) * 16 + tr;
-          const floatx4 v = ytile[wave][tr][lc];
-          if (r < cnt && col_in) {
-            const size_t yi = (size_t)(row0 + r) * H + n0 + 4 * lc;
-            if constexpr (Y24) store_y24(y, yi, v);
-            else store_y4<FP8>(y, yi, v);
+          for (int q = 0; q < 4; ++q) {
+            const int tr = 4 * q + lr;
+            const int r = (t0 + mt) * 16 + tr;
+            const floatx4 v = ytile[wave][tr][lc];
+            if (r < cnt && col_in) {
+              const size_t yi = (size_t)(row0 + r) * H + n0 + 4 * lc;
+              if constexpr (Y24) store_y24(y, yi, v);
+              else store_y4<FP8>(y, yi, v);
+            }
           }
         }
       }
     }
+    // the unit's rows (one 64-row block of the segment) x its 256 columns
+    if (bs.sig != nullptr)
+      signal_rows_done(bs, e, it * kStreamItemRows, min(kStreamItemRows, cnt - it * kStreamItemRows),
+                       min(256, H - ngb * 256));
   }
 }
 
@@ -728,13 +735,14 @@ struct DnArgs {
   const int32_t* n_items;
   void* y;
   int H, I, max_items, n_ng;
+  BlockSignals bs;
 };
 
 template <int KU, bool FP8, bool PW, bool Y24>
 void launch_dn(const DnArgs& a) {
   hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW, Y24>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
                      a.s2, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0, a.n_items, a.y, a.H,
-                     a.I, a.max_items, a.n_ng);
+                     a.I, a.max_items, a.n_ng, a.bs);
 }
 
 template <bool FP8, bool PW, bool Y24 = false>
@@ -826,8 +834,9 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
-                       int bm, int max_rows, bool y24, hipStream_t s) {
+                       int bm, int max_rows, bool y24, hipStream_t s, BlockSignals bs) {
   if (wkind == W_F32) {
+    if (bs.sig != nullptr) return hipErrorInvalidValue;
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
                        block_expert, n_post, static_cast<float*>(y), H, I, bm);
@@ -838,7 +847,7 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
   const int n_ng = (H + 255) / 256;
   if ((long long)max_items * n_ng > INT_MAX - 8) return hipErrorInvalidValue;
   DnArgs a{dim3(stream_grid(max_items * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2,
-           seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng};
+           seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng, bs};
   if (fp8) {
     if (packed) launch_dn_ku<true, true>(ku, a);
     else launch_dn_ku<true, false>(ku, a);

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(
     const int32_t* __restrict__ tile_row0, const int32_t* __restrict__ n_tiles_ptr,
     const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
     const uint8_t* __restrict__ valid, void* __restrict__ dst, int H, int I, int n_nt,
-    int max_tiles, int T, int E, int ksplit) {
+    int max_tiles, int T, int E, int ksplit, BlockSignals bs) {
   __shared__ u32x4 abuf[2][kASlots][kWave];   // 2 x 16 KB
   __shared__ u32x4 bbuf[2][kBSlots][kWave];   // 2 x 32 KB
   __shared__ float sscale[2][kMaxScaleCols];  // fp8: the two 128-row scale rows
@@ -314,6 +314,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(
           static_cast<float*>(dst)[(size_t)z * T * E + ro + n] = acc[mt][q][i];
       }
     }
+  if constexpr (OP == OP_DOWN) {
+    // the tile's rows x its kBN columns
+    if (bs.sig != nullptr)
+      signal_rows_done(bs, e, tile_row0[mt_id], rows_here, min(kBN, H - nt * kBN));
+  }
 }
 
 // 8 fp8 codes (two dwords) -> 8 bf16 of value(q) * s, rounded to nearest even
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, float* __restrict__ y, int H, int n_chunks,
-    int max_tiles) {
+    int max_tiles, BlockSignals bs) {
   constexpr int I = 32 * KSTEPS;
   __shared__ u32x4 hbuf[8 * KSTEPS][kWave];   // (row tile, step) slots, 1 KB each
   const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
@@ -426,25 +431,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       store_y8<false>(y, (size_t)(row_base + row) * H + nh + 8 * g, acc[0][mt], acc[1][mt]);
     }
   };
-  if (tile_n0(0) >= H) return;
-  preload(tile_n0(0));
-  // scheduling barriers keep each half's loads, MFMAs and stores in their
-  // phase (hoisting the later loads spills registers)
-  for (int t = 0; t < kTallCPW; ++t) {
-    const int n0 = tile_n0(t);
-    half();
-    __builtin_amdgcn_sched_barrier(0);
-    preload(n0 + 32);
-    store(n0);
-    __builtin_amdgcn_sched_barrier(0);
-    half();
-    __builtin_amdgcn_sched_barrier(0);
-    const bool more = t + 1 < kTallCPW && tile_n0(t + 1) < H;
-    if (more) preload(tile_n0(t + 1));
-    store(n0 + 32);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!more) break;
+  if (tile_n0(0) < H) {
+    preload(tile_n0(0));
+    // scheduling barriers keep each half's loads, MFMAs and stores in their
+    // phase (hoisting the later loads spills registers)
+    for (int t = 0; t < kTallCPW; ++t) {
+      const int n0 = tile_n0(t);
+      half();
+      __builtin_amdgcn_sched_barrier(0);
+      preload(n0 + 32);
+      store(n0);
+      __builtin_amdgcn_sched_barrier(0);
+      half();
+      __builtin_amdgcn_sched_barrier(0);
+      const bool more = t + 1 < kTallCPW && tile_n0(t + 1) < H;
+      if (more) preload(tile_n0(t + 1));
+      store(n0 + 32);
+      __builtin_amdgcn_sched_barrier(0);
+      if (!more) break;
+    }
   }
+  if (bs.sig != nullptr)
+    signal_rows_done(bs, e, r0, rows_here, min(256 * kTallCPW, H - c_beg));
 }
 
 // The same down projection for fp8 W2.  A wave takes a 64-column tile in two
@@ -574,7 +582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int32_t* __restrict__ tile_seg, const int32_t* __restrict__ tile_row0,
     const int32_t* __restrict__ n_tiles_ptr, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, uint16_t* __restrict__ y, int H, int n_chunks,
-    int max_tiles) {
+    int max_tiles, BlockSignals bs) {
   __shared__ u32x4 hbuf[8 * KSTEPS][kWave];
   const int lid = live_block_g(min(*n_tiles_ptr, max_tiles) * n_chunks);
   if (lid < 0) return;
@@ -587,6 +595,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     down_f8s_tile<KSTEPS, PW, 1>(h, w2, s2, y, H, e, ch, row_base, rows_here, hbuf);
   else
     down_f8s_tile<KSTEPS, PW, 2>(h, w2, s2, y, H, e, ch, row_base, rows_here, hbuf);
+  if (bs.sig != nullptr)
+    signal_rows_done(bs, e, r0, rows_here, min(256 * kTallCPW, H - ch * 256 * kTallCPW));
 }
 
 // Gate/up of the large segments: 128 sorted rows x (128 gate + the matching
@@ -1123,18 +1133,18 @@ template <int OP, bool FP8, bool PW>
 void launch_gemm(dim3 grid, hipStream_t s, const uint16_t* a, const void* w, const float* ws,
                  const int32_t* tseg, const int32_t* trow, const int32_t* ntiles,
                  const int32_t* seg_off, const int32_t* seg_cnt, void* dst, int H, int I,
-                 int n_nt, int max_tiles) {
+                 int n_nt, int max_tiles, BlockSignals bs) {
   hipLaunchKernelGGL((gemm_kernel<OP, FP8, PW>), grid, dim3(256), 0, s, a, w, ws, tseg, trow,
-                     ntiles, seg_off, seg_cnt, nullptr, dst, H, I, n_nt, max_tiles, 0, 0, 1);
+                     ntiles, seg_off, seg_cnt, nullptr, dst, H, I, n_nt, max_tiles, 0, 0, 1, bs);
 }
 
 template <int OP>
 void launch_gemm_w(bool fp8, bool packed, dim3 grid, hipStream_t s, const uint16_t* a,
                    const void* w, const float* ws, const int32_t* tseg, const int32_t* trow,
                    const int32_t* ntiles, const int32_t* seg_off, const int32_t* seg_cnt,
-                   void* dst, int H, int I, int n_nt, int max_tiles) {
+                   void* dst, int H, int I, int n_nt, int max_tiles, BlockSignals bs) {
 #define MOE_GEMM_ARGS grid, s, a, w, ws, tseg, trow, ntiles, seg_off, seg_cnt, dst, H, I, n_nt, \
-                      max_tiles
+                      max_tiles, bs
   if (fp8) {
     if (packed) launch_gemm<OP, true, true>(MOE_GEMM_ARGS);
     else launch_gemm<OP, true, false>(MOE_GEMM_ARGS);
@@ -1187,7 +1197,7 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
                             const float* s2, const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
                             const int32_t* seg_cnt, void* y, int H, int I, int max_tiles,
-                            hipStream_t s) {
+                            hipStream_t s, BlockSignals bs) {
   if (I % 128 != 0 || I > kMaxGemmK) return hipErrorInvalidValue;
   if (I == 128 || I == 256) {
     const int n_chunks = (H + 256 * kTallCPW - 1) / (256 * kTallCPW);
@@ -1196,11 +1206,11 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
 #define MOE_TALL(KS, P)                                                                     \
   hipLaunchKernelGGL((down_tall_kernel<KS, P>), grid, dim3(256), 0, s, hb,                    \
                      static_cast<const uint16_t*>(w2), tile_seg, tile_row0, n_tiles, seg_off,  \
-                     seg_cnt, static_cast<float*>(y), H, n_chunks, max_tiles)
+                     seg_cnt, static_cast<float*>(y), H, n_chunks, max_tiles, bs)
 #define MOE_TALL8(KS, P)                                                                    \
   hipLaunchKernelGGL((down_tall_f8s_kernel<KS, P>), grid, dim3(256), 0, s, hb,                \
                      static_cast<const uint8_t*>(w2), s2, tile_seg, tile_row0, n_tiles, seg_off, \
-                     seg_cnt, static_cast<uint16_t*>(y), H, n_chunks, max_tiles)
+                     seg_cnt, static_cast<uint16_t*>(y), H, n_chunks, max_tiles, bs)
     if (I == 128) {
       if (fp8) { if (packed) MOE_TALL8(4, true); else MOE_TALL8(4, false); }
       else { if (packed) MOE_TALL(4, true); else MOE_TALL(4, false); }
@@ -1215,7 +1225,7 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
   const int n_nt = (H + kBN - 1) / kBN;
   launch_gemm_w<OP_DOWN>(fp8, packed, dim3(round8g(max_tiles * n_nt)), s,
                          static_cast<const uint16_t*>(h), w2, s2, tile_seg, tile_row0, n_tiles,
-                         seg_off, seg_cnt, y, H, I, n_nt, max_tiles);
+                         seg_off, seg_cnt, y, H, I, n_nt, max_tiles, bs);
   return hipGetLastError();
 }
 
@@ -1237,7 +1247,8 @@ hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R
   dim3 grid(round8g(tiles * n_nt * ks));
   hipLaunchKernelGGL((gemm_kernel<OP_ROUTER, false, false>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), R, nullptr, nullptr, nullptr, nullptr,
-                     nullptr, nullptr, valid, part, H, 0, n_nt, tiles, T, E, ks);
+                     nullptr, nullptr, valid, part, H, 0, n_nt, tiles, T, E, ks,
+                     BlockSignals{nullptr, 0});
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #include "moe_kernels.h"
 
 #include <algorithm>
+#include <climits>
 
 namespace moe {
 namespace {
@@ -157,14 +158,106 @@ __device__ __forceinline__ bool combine_slots(const int32_t* ids, const float* w
   return valid;
 }
 
-// fp32 y rows, or 24-bit ones (Y24); y is read once: non-temporal loads
-template <int NV, bool Y24>
-__global__ __launch_bounds__(256) void combine_kernel(
+// Wave 0 of a waiting combine block: wait until the completion counters of
+// the blocks that hold the assignments of rows [t0, t1) (padding rows have
+// none) reach cw.target, then acquire at agent scope, so that the y rows the
+// producers stored before their release are the ones read.  Lane l polls
+// pairs (row, slot) l, l + 64, ...; the shared slot's block is in segment E.
+// False when the wait ran out of time or an earlier one did.
+__device__ bool wait_rows(const CombineWait& cw, const int32_t* ids, const int32_t* slot_pos,
+                          int t0, int t1, int k, int kk) {
+  const int lane = threadIdx.x;
+  const int n_pairs = (t1 - t0) * kk;
+  const uint64_t start = __builtin_amdgcn_s_memrealtime();
+  for (int q0 = 0; q0 < n_pairs; q0 += kWave) {
+    const int q = q0 + lane;
+    const int32_t* c = nullptr;
+    if (q < n_pairs) {
+      const int t = t0 + q / kk, j = q % kk;
+      if (ids[(size_t)t * k] >= 0) {
+        const int e = j < k ? ids[(size_t)t * k + j] : cw.E;
+        const int p = slot_pos[(size_t)t * kk + j];
+        c = cw.sig + (size_t)e * cw.nb64 + ((p - cw.seg_off[e]) >> 6);
+      }
+    }
+    for (;;) {
+      const bool ready =
+          c == nullptr ||
+          __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cw.target;
+      if (__all(ready)) break;
+      if (__any(__hip_atomic_load(cw.giveup, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0))
+        return false;
+      if (__builtin_amdgcn_s_memrealtime() - start > (uint64_t)cw.ticks) {
+        if (lane == 0)
+          __hip_atomic_store(cw.giveup, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// The waiting combine runs as a persistent grid of at most kWaitGrid blocks
+// (one per CU), each taking groups of rows in row order, T / kWaitGrid rows
+// per group but at least one and at most kWaitRows: one wait and one acquire
+// per group.  A block per (row, column chunk), as the other
+// modes launch, filled every CU slot with waiting blocks and starved the
+// down kernels they wait for (prefill micro-batch: down GEMM 375 us -> 10 ms,
+// until the waits ran out); an acquire per row invalidated the L2 so often
+// that the down GEMM, whose tiles share W2 through it, ran at half speed.
+constexpr int kWaitGrid = 256;
+constexpr int kWaitRows = 32;
+__host__ __device__ inline int wait_group_rows(int T) {
+  return T / kWaitGrid < 1 ? 1 : (T / kWaitGrid > kWaitRows ? kWaitRows : T / kWaitGrid);
+}
+
+// Called by every thread of a COMBINE_WAIT block: true when the block may
+// combine rows [t0, t1).  The caller passes a barrier before the next call.
+__device__ bool wait_group(const CombineWait& cw, const int32_t* ids, const int32_t* slot_pos,
+                           int t0, int t1, int k, int kk) {
+  __shared__ int s_ok;
+  if (threadIdx.x < kWave) {
+    const bool ok = wait_rows(cw, ids, slot_pos, t0, t1, k, kk);
+    if (threadIdx.x == 0) s_ok = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return s_ok != 0;
+}
+
+// The persistent loop of the waiting combine: part(t, by) combines column
+// chunk by of row t; done flags are set for the rows combined.
+template <typename Part>
+__device__ __forceinline__ void wait_and_combine(const CombineWait& cw, const int32_t* ids,
+                                                 const int32_t* slot_pos, int T, int k, int kk,
+                                                 int gy, Part part) {
+  const int rows = wait_group_rows(T);
+  for (int t0 = blockIdx.x * rows; t0 < T; t0 += gridDim.x * rows) {
+    const int t1 = min(T, t0 + rows);
+    if (wait_group(cw, ids, slot_pos, t0, t1, k, kk)) {
+      for (int t = t0; t < t1; ++t)
+        for (int by = 0; by < gy; ++by) part(t, by);
+      for (int i = threadIdx.x; i < (t1 - t0) * gy; i += blockDim.x)
+        cw.done[(size_t)t0 * gy + i] = 1;
+    }
+    __syncthreads();
+  }
+}
+
+// fp32 y rows, or 24-bit ones (Y24); y is read once: non-temporal loads.
+// Part `by` of the gy column chunks of row t; MODE: COMBINE_ALL, or
+// COMBINE_REST (skip a part whose done flag is set).
+template <int NV, bool Y24, int MODE>
+__device__ __forceinline__ void combine_part(
     const void* __restrict__ y, const int32_t* __restrict__ ids,
-    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
-    int H, int k, int ns, void* __restrict__ out, int out_bf16) {
-  const int t = blockIdx.x;
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos,
+    int H, int k, int ns, void* __restrict__ out, int out_bf16, const CombineWait& cw, int t,
+    int by, int gy) {
   const int kk = k + ns;
+  if constexpr (MODE == COMBINE_REST) {
+    if (cw.done[(size_t)t * gy + by] != 0) return;
+  }
   int pos[kMaxSlots];
   float wt[kMaxSlots];
   const bool valid = combine_slots(ids, w, slot_pos, t, k, kk, pos, wt);
@@ -174,7 +267,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
   floatx4 acc[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    n[v] = ((blockIdx.y * NV + v) * 256 + threadIdx.x) * 4;
+    n[v] = ((by * NV + v) * 256 + threadIdx.x) * 4;
     acc[v] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   if (valid) {
@@ -214,14 +307,36 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+template <int NV, bool Y24, int MODE>
+__global__ __launch_bounds__(256) void combine_kernel(
+    const void* __restrict__ y, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T,
+    int H, int k, int ns, void* __restrict__ out, int out_bf16, CombineWait cw, int gy) {
+  if constexpr (MODE == COMBINE_WAIT) {
+    wait_and_combine(cw, ids, slot_pos, T, k, k + ns, gy, [&](int t, int by) {
+      combine_part<NV, Y24, COMBINE_ALL>(y, ids, w, slot_pos, H, k, ns, out, out_bf16, cw, t,
+                                         by, gy);
+    });
+  } else {
+    combine_part<NV, Y24, MODE>(y, ids, w, slot_pos, H, k, ns, out, out_bf16, cw, blockIdx.x,
+                                blockIdx.y, gridDim.y);
+  }
+}
+
 // bf16 y rows (fp8-weight layers), bf16 out: 8 columns per thread, 16-byte
-// non-temporal y loads, all issued before the sums.
-__global__ __launch_bounds__(256) void combine_ybf_kernel(
+// non-temporal y loads, all issued before the sums.  Part `by` of the gy
+// column chunks of row t; MODE: COMBINE_ALL or COMBINE_REST.
+template <int MODE>
+__device__ __forceinline__ void combine_ybf_part(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
     const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int H, int k, int ns,
-    uint16_t* __restrict__ out) {
-  const int t = blockIdx.x, kk = k + ns;
-  const int n = (blockIdx.y * 256 + threadIdx.x) * 8;
+    uint16_t* __restrict__ out, const CombineWait& cw, int t, int by, int gy) {
+  const int kk = k + ns;
+  const int n = (by * 256 + threadIdx.x) * 8;
+  if constexpr (MODE == COMBINE_REST) {
+    if (cw.done[(size_t)t * gy + by] != 0) return;
+  }
+
   if (n >= H) return;   // H % 8 == 0: a thread's 8 columns are all in range
   int pos[kMaxSlots];
   float wt[kMaxSlots];
@@ -251,6 +366,21 @@ __global__ __launch_bounds__(256) void combine_ybf_kernel(
   for (int q = 0; q < 4; ++q)
     pk[q] = (uint32_t)f32_to_bf16_bits(acc[2 * q]) | ((uint32_t)f32_to_bf16_bits(acc[2 * q + 1]) << 16);
   *reinterpret_cast<u32x4*>(out + (size_t)t * H + n) = pk;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void combine_ybf_kernel(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ ids,
+    const float* __restrict__ w, const int32_t* __restrict__ slot_pos, int T, int H, int k,
+    int ns, uint16_t* __restrict__ out, CombineWait cw, int gy) {
+  if constexpr (MODE == COMBINE_WAIT) {
+    wait_and_combine(cw, ids, slot_pos, T, k, k + ns, gy, [&](int t, int by) {
+      combine_ybf_part<COMBINE_ALL>(y, ids, w, slot_pos, H, k, ns, out, cw, t, by, gy);
+    });
+  } else {
+    combine_ybf_part<MODE>(y, ids, w, slot_pos, H, k, ns, out, cw, blockIdx.x, blockIdx.y,
+                           gridDim.y);
+  }
 }
 
 }  // namespace
@@ -295,15 +425,33 @@ hipError_t launch_pack_weights(int wkind, const void* src, void* dst, size_t row
   return hipGetLastError();
 }
 
+int combine_grid_y(int T, int H, int yfmt) {
+  if (yfmt == Y_BF16) return (H + 2047) / 2048;
+  const int nv = T >= 2048 ? 8 : (T >= 256 ? 2 : 1);
+  return (H + 1024 * nv - 1) / (1024 * nv);
+}
+
 hipError_t launch_combine(const void* y, int yfmt, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
-                          hipStream_t s) {
+                          hipStream_t s, int mode, const CombineWait* cw) {
+  if (mode != COMBINE_ALL && cw == nullptr) return hipErrorInvalidValue;
+  const CombineWait cwv = cw != nullptr ? *cw : CombineWait{};
+  const int gy = combine_grid_y(T, H, yfmt);
+  if ((long long)T * gy > INT_MAX) return hipErrorInvalidValue;
+  // the waiting combine: a persistent grid over groups of rows
+  const int groups = (T + wait_group_rows(T) - 1) / wait_group_rows(T);
+  const dim3 grid = mode == COMBINE_WAIT ? dim3(std::min(groups, kWaitGrid)) : dim3(T, gy);
   if (yfmt == Y_BF16) {
     if (!out_bf16 || H % 8 != 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(combine_ybf_kernel, dim3(T, (H + 2047) / 2048), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(y), ids, w, slot_pos, H, k, n_shared,
-                       static_cast<uint16_t*>(out));
+#define MOE_COMBINE_BF(MODE)                                                                  \
+  hipLaunchKernelGGL(combine_ybf_kernel<MODE>, grid, dim3(256), 0, s,                          \
+                     static_cast<const uint16_t*>(y), ids, w, slot_pos, T, H, k, n_shared,      \
+                     static_cast<uint16_t*>(out), cwv, gy)
+    if (mode == COMBINE_WAIT) MOE_COMBINE_BF(COMBINE_WAIT);
+    else if (mode == COMBINE_REST) MOE_COMBINE_BF(COMBINE_REST);
+    else MOE_COMBINE_BF(COMBINE_ALL);
+#undef MOE_COMBINE_BF
     return hipGetLastError();
   }
   if (yfmt != Y_F32 && yfmt != Y_F24) return hipErrorInvalidValue;
@@ -312,18 +460,43 @@ hipError_t launch_combine(const void* y, int yfmt, const int32_t* ids, const flo
   // of the blocks, each with 4x the loads in flight (gather_padded_e48, 86%
   // padding rows that only take zeros: 57.8 -> 50.5 us)
   const int ob = out_bf16 ? 1 : 0;
-#define MOE_COMBINE(NV, Y24)                                                                  \
-  hipLaunchKernelGGL((combine_kernel<NV, Y24>), dim3(T, (H + 1024 * NV - 1) / (1024 * NV)),    \
-                     dim3(256), 0, s, y, ids, w, slot_pos, T, H, k, n_shared, out, ob)
+#define MOE_COMBINE(NV, Y24, MODE)                                                            \
+  hipLaunchKernelGGL((combine_kernel<NV, Y24, MODE>), grid, dim3(256), 0, s, y, ids, w,         \
+                     slot_pos, T, H, k, n_shared, out, ob, cwv, gy)
+#define MOE_COMBINE_M(NV, Y24)                                                               \
+  if (mode == COMBINE_WAIT) MOE_COMBINE(NV, Y24, COMBINE_WAIT);                               \
+  else if (mode == COMBINE_REST) MOE_COMBINE(NV, Y24, COMBINE_REST);                          \
+  else MOE_COMBINE(NV, Y24, COMBINE_ALL)
   const bool y24 = yfmt == Y_F24;
   if (T >= 2048) {
-    if (y24) MOE_COMBINE(8, true); else MOE_COMBINE(8, false);
+    if (y24) { MOE_COMBINE_M(8, true); } else { MOE_COMBINE_M(8, false); }
   } else if (T >= 256) {
-    if (y24) MOE_COMBINE(2, true); else MOE_COMBINE(2, false);
+    if (y24) { MOE_COMBINE_M(2, true); } else { MOE_COMBINE_M(2, false); }
   } else {
-    if (y24) MOE_COMBINE(1, true); else MOE_COMBINE(1, false);
+    if (y24) { MOE_COMBINE_M(1, true); } else { MOE_COMBINE_M(1, false); }
   }
+#undef MOE_COMBINE_M
 #undef MOE_COMBINE
+  return hipGetLastError();
+}
+
+namespace {
+// Zero two int32 ranges.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ a, size_t na,
+                                                       int32_t* __restrict__ b, size_t nb) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += stride) {
+    if (i < na) a[i] = 0;
+    else b[i - na] = 0;
+  }
+}
+}  // namespace
+
+hipError_t launch_zero_i32(int32_t* a, size_t na, int32_t* b, size_t nb, hipStream_t s) {
+  const size_t n = na + nb;
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(grid), dim3(256), 0, s, a, na, b, nb);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ struct Plan {
   int max_items;  // bound on the streaming kernels' work items
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
       off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_iseg, off_irow, off_nitems,
-      off_span, off_h, off_y, off_xq, off_sx, total;
+      off_span, off_h, off_y, off_xq, off_sx, off_done, total;
   bool xsplit;    // fp8 weights on the GEMM path: token rows as two e4m3 terms
   int yfmt;       // format of the expert output rows y (moe::YFmt)
   bool down_cols; // down projection and combine in one launch (small batches)
@@ -89,6 +89,16 @@ int check_desc(const moe_desc* d, int32_t topk, bool need_scales = true) {
   if ((unsigned long long)rows * (unsigned long long)d->I >= (1ULL << 32))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// Column chunks per row that the combine grid can have (the done flags of
+// the waiting combine).
+int done_chunks(int H) { return (H + 1023) / 1024; }
+
+// Completion counters of moe_forward_signaled: (E + n_shared) segments x
+// ceil(T / 64) blocks.
+size_t signal_count(const moe_desc* d) {
+  return (size_t)(d->E + d->n_shared) * (size_t)((d->T + 63) / 64);
 }
 
 // The tiled kernels index x with 32-bit element offsets.
@@ -190,6 +200,9 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   p->xsplit = xq_room && p->big_thr != INT_MAX;
   p->off_xq = take(xq_room ? (size_t)2 * p->T * p->H : 0);
   p->off_sx = take(xq_room ? (size_t)p->T * 4 : 0);
+  // done flags of the waiting combine (moe_forward_signaled): one per (row,
+  // column chunk of the combine grid), then the give-up flag
+  p->off_done = take(((size_t)p->T * done_chunks(p->H) + 1) * 4);
   p->total = o;
   return MOE_OK;
 }
@@ -202,10 +215,11 @@ T* at(void* ws, size_t off) {
 // ---- measurement hooks -------------------------------------------------------
 enum Stage {
   S_LOGITS = 0, S_TOPK, S_ALIGN, S_PACK_X, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM,
-  S_COMBINE, S_X_SPLIT, S_COUNT
+  S_COMBINE, S_X_SPLIT, S_COMBINE_WAIT, S_COUNT
 };
 const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "pack_x", "gate_up",
-                                    "gate_up_gemm", "down", "down_gemm", "combine", "x_split"};
+                                    "gate_up_gemm", "down", "down_gemm", "combine", "x_split",
+                                    "combine_wait"};
 
 struct ProfRecord {
   int stage;
@@ -244,11 +258,43 @@ hipError_t launch_logits(const Plan& p, const void* x, const uint8_t* valid,
                                   p.ks, s);
 }
 
+// moe_forward_signaled: the caller's completion counters and the stream of
+// the waiting combine.
+struct SignalCtx {
+  int32_t* sig;
+  hipStream_t consumer;
+};
+
+// Events of one signaled call, created with it and released once its waits
+// are enqueued (HIP frees an event whose record is pending when that
+// completes).
+struct CallEvents {
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  ~CallEvents() {
+    for (hipEvent_t e : ev)
+      if (e != nullptr) (void)hipEventDestroy(e);
+  }
+  bool make() {
+    for (hipEvent_t& e : ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return false;
+    return true;
+  }
+};
+
+// Time bound of one wait of the waiting combine, in microseconds
+// (moe_set_signal_wait_us; the kernels count 100 MHz real-time ticks): 10 ms
+// by default, far above any down projection it waits for.  A wait that runs
+// out hands its rows to the rest pass.
+std::atomic<int> g_wait_us{10000};
+
 // The launch sequence of one layer forward into a workspace of p.total bytes
-// (arguments already validated).
+// (arguments already validated).  With sc, the down kernels raise the
+// per-(segment, 64-row block) completion counters sc->sig and the combine
+// runs on sc->consumer as their consumer (COMBINE_WAIT), followed on s by
+// the rest pass for whatever it left.
 int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8_t* valid_rows,
                  const void* router_w, const void* w13, const void* w2, void* out,
-                 void* workspace, hipStream_t s) {
+                 void* workspace, hipStream_t s, const SignalCtx* sc = nullptr) {
   void* ws = workspace;
   float* part = at<float>(ws, p.off_part);
   int32_t* ids = at<int32_t>(ws, p.off_ids);
@@ -305,6 +351,13 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                             p.cap, !gemm, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
+  // the counters and the done flags start at zero in every signaled call
+  const int nb64 = (p.T + 63) / 64;
+  int32_t* done = at<int32_t>(ws, p.off_done);
+  const size_t n_done = (size_t)p.T * done_chunks(p.H);
+  if (sc != nullptr &&
+      moe::launch_zero_i32(sc->sig, (size_t)(p.E + p.ns) * nb64, done, n_done + 1, s) != hipSuccess)
+    return MOE_ERR_HIP;
   uint8_t* xq = p.xsplit ? at<uint8_t>(ws, p.off_xq) : nullptr;
   float* sx = p.xsplit ? at<float>(ws, p.off_sx) : nullptr;
   if (p.xsplit) {
@@ -318,6 +371,11 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                                  p.T, s) != hipSuccess)
       return MOE_ERR_HIP;
   }
+  // signaled calls: the waiting combine may start once h is complete
+  CallEvents evs;
+  if (sc != nullptr && (!evs.make() || hipEventRecord(evs.ev[0], s) != hipSuccess))
+    return MOE_ERR_HIP;
+  const moe::BlockSignals bs{sc != nullptr ? sc->sig : nullptr, nb64};
   if (p.down_cols) {
     // the down projection and the combine in one launch
     StageTimer tm(S_DOWN, s);
@@ -330,14 +388,33 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
     StageTimer tm(S_DOWN, s);
     if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
                          irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap, p.yfmt == moe::Y_F24,
-                         s) != hipSuccess)
+                         s, bs) != hipSuccess)
       return MOE_ERR_HIP;
   }
   if (gemm) {
     StageTimer tm(S_DOWN_GEMM, s);
     if (moe::launch_down_gemm(wkind == moe::W_FP8, packed, h, w2, desc->w2_scale, tseg, trow, ntiles,
-                              offs, cnt, y, p.H, p.I, p.max_tiles, s) != hipSuccess)
+                              offs, cnt, y, p.H, p.I, p.max_tiles, s, bs) != hipSuccess)
       return MOE_ERR_HIP;
+  }
+  if (sc != nullptr) {
+    const moe::CombineWait cw{sc->sig, offs, nb64, p.H, p.E, done, done + n_done,
+                              100LL * g_wait_us.load()};
+    if (hipStreamWaitEvent(sc->consumer, evs.ev[0], 0) != hipSuccess) return MOE_ERR_HIP;
+    {
+      StageTimer tm(S_COMBINE_WAIT, sc->consumer);
+      if (moe::launch_combine(y, p.yfmt, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+                              p.act == MOE_BF16, sc->consumer, moe::COMBINE_WAIT, &cw) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+    if (hipEventRecord(evs.ev[1], sc->consumer) != hipSuccess ||
+        hipStreamWaitEvent(s, evs.ev[1], 0) != hipSuccess)
+      return MOE_ERR_HIP;
+    StageTimer tm(S_COMBINE, s);
+    if (moe::launch_combine(y, p.yfmt, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+                            p.act == MOE_BF16, s, moe::COMBINE_REST, &cw) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
   }
   {
     StageTimer tm(S_COMBINE, s);
@@ -404,6 +481,12 @@ int moe_set_path_thresholds(int32_t gemm_min_rows, int32_t gemm_min_tiles) {
   if (gemm_min_rows < 0 || gemm_min_tiles < -1) return MOE_ERR_INVALID_ARG;
   g_gemm_min_rows.store(gemm_min_rows);
   g_gemm_min_tiles.store(gemm_min_tiles);
+  return MOE_OK;
+}
+
+int moe_set_signal_wait_us(int32_t us) {
+  if (us < 0 || us > 1000000) return MOE_ERR_INVALID_ARG;
+  g_wait_us.store(us);
   return MOE_OK;
 }
 
@@ -484,6 +567,32 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   return forward_impl(p, desc, x, valid_rows, router_w, w13, w2, out, workspace,
                       static_cast<hipStream_t>(stream));
+}
+
+size_t moe_block_signal_count(const moe_desc* desc) {
+  if (desc == nullptr || desc->T < 1 || desc->E < 1 || desc->n_shared < 0) return 0;
+  return signal_count(desc);
+}
+
+int moe_forward_signaled(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                         const void* router_w, const void* w13, const void* w2, int32_t topk,
+                         void* out, void* workspace, size_t workspace_bytes,
+                         int32_t* block_signal, moe_stream_t stream,
+                         moe_stream_t consumer_stream) {
+  Plan p;
+  const int st = make_plan(desc, topk, &p);
+  if (st != MOE_OK) return st;
+  if (!x || !router_w || !w13 || !w2 || !out || !workspace || !block_signal)
+    return MOE_ERR_INVALID_ARG;
+  // the fp32 kernels raise no signals
+  if (p.w == MOE_F32 || p.act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+  // the per-assignment y rows are the signals' subject: no one-launch down +
+  // combine
+  p.down_cols = false;
+  const SignalCtx sc{block_signal, static_cast<hipStream_t>(consumer_stream)};
+  return forward_impl(p, desc, x, valid_rows, router_w, w13, w2, out, workspace,
+                      static_cast<hipStream_t>(stream), &sc);
 }
 
 int moe_forward_noalloc(const moe_desc* desc, const void* x, const uint8_t* valid_rows,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_kernels.h"
+
 namespace moe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -130,6 +132,23 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ u32x2 ld8(const void* p) {
   return *reinterpret_cast<const u32x2*>(p);
+}
+
+// Raises the completion signals (BlockSignals) of a down-projection unit.
+// Called by every thread of a block once the block has stored ncols columns
+// of y for rows [r0, r0 + nrows) of segment seg (r0 a multiple of 64).  Each
+// wave waits for its own stores, then one release at agent scope (the write
+// back of this XCD's L2) orders all of them before the counts grow.
+__device__ __forceinline__ void signal_rows_done(BlockSignals bs, int seg, int r0, int nrows,
+                                                 int ncols) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0 && nrows > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int b = r0 >> 6; b <= (r0 + nrows - 1) >> 6; ++b)
+      __hip_atomic_fetch_add(bs.sig + (size_t)seg * bs.nb64 + b, ncols, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // MFMA fragment order of a [rows, K] bf16 matrix in 16-row tiles: tile t

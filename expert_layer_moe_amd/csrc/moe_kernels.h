@@ -6,6 +6,34 @@
 
 namespace moe {
 
+// Completion signals of the expert output rows y, one counter per (segment,
+// 64-row block of the segment) ("[SGLang] Single Batch Overlap for MoE
+// models", combine-signal section: the down-projection GEMM reports each
+// finished block so that its consumer can start on it).  sig[seg * nb64 + b]
+// counts the columns of y stored for rows 64 b .. 64 b + 63 of segment seg;
+// the block is complete when the count reaches H.  The down launchers raise
+// them when sig is non-null (the counters must start at zero).
+struct BlockSignals {
+  int32_t* sig;   // null: the launch raises no signals
+  int nb64;       // counters per segment: ceil(T / 64)
+};
+
+// The combine as the signals' consumer.  COMBINE_WAIT: each block waits
+// (wave 0, bounded in time) until the counters of its row's assignments
+// reach target, then combines that part of the row and sets its done flag;
+// a wait that runs out of time sets *giveup, after which no block waits and
+// rows are left undone.  COMBINE_REST: combine only the parts whose done
+// flag is 0 (launched once the producer and the waiting combine have ended).
+enum CombineMode { COMBINE_ALL = 0, COMBINE_WAIT = 1, COMBINE_REST = 2 };
+struct CombineWait {
+  const int32_t* sig;       // BlockSignals counters
+  const int32_t* seg_off;   // segment starts in the sorted row list
+  int nb64, target, E;      // target: H; E: the shared segment's index
+  int32_t* done;            // [T][combine_grid_y]: zeroed before the producer runs
+  int32_t* giveup;          // zeroed likewise
+  long long ticks;          // time bound of one wait, in 100 MHz real-time ticks
+};
+
 // ---- route -----------------------------------------------------------------
 // Partial router logits: part[z][t][e] = sum over the z-th K chunk of
 // x[t,:] * R[e,:].  bf16 inputs use MFMA; fp32 inputs use a plain FMA loop
@@ -102,7 +130,7 @@ hipError_t launch_down_gemm(bool fp8, bool packed, const void* h, const void* w2
                             const int32_t* tile_seg, const int32_t* tile_row0,
                             const int32_t* n_tiles, const int32_t* seg_off,
                             const int32_t* seg_cnt, void* y, int H, int I, int max_tiles,
-                            hipStream_t s);
+                            hipStream_t s, BlockSignals bs = BlockSignals{nullptr, 0});
 // Router GEMM: part[z][t][e] for K chunk z of ks (H % (128 ks) == 0); tiles
 // with no valid row are skipped (their partials are never read).
 hipError_t launch_router_gemm(const void* x, const uint8_t* valid, const void* R,
@@ -124,7 +152,8 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
-                       int bm, int max_rows, bool y24, hipStream_t s);
+                       int bm, int max_rows, bool y24, hipStream_t s,
+                       BlockSignals bs = BlockSignals{nullptr, 0});
 // Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
 // K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
 // s) of 512 elements at (t K/32 + s) 512, lane 16 g + m holding row 16 t + m,
@@ -138,6 +167,11 @@ enum YFmt { Y_F32 = 0, Y_BF16 = 1, Y_F24 = 2 };
 hipError_t launch_combine(const void* y, int yfmt, const int32_t* ids, const float* w,
                           const int32_t* slot_pos, int T, int H, int k,
                           int n_shared, void* out, bool out_bf16,
-                          hipStream_t s);
+                          hipStream_t s, int mode = COMBINE_ALL,
+                          const CombineWait* cw = nullptr);
+// Column chunks per row of the combine grid (at most (H + 1023) / 1024).
+int combine_grid_y(int T, int H, int yfmt);
+// a[0 .. na) = 0 and b[0 .. nb) = 0 (a fill kernel: safe under graph capture)
+hipError_t launch_zero_i32(int32_t* a, size_t na, int32_t* b, size_t nb, hipStream_t s);
 
 }  // namespace moe

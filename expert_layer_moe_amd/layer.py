@@ -8,7 +8,7 @@ import torch
 
 from .binding import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_LAYOUT_FRAG16,
                       MOE_LAYOUT_ROW_MAJOR, alloc_workspace, make_desc, moe_forward,
-                      moe_pack_weights, moe_route)
+                      moe_forward_signaled, moe_pack_weights, moe_route)
 
 _ACT = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 _W = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16, torch.uint8: MOE_FP8_E4M3}
@@ -69,6 +69,24 @@ class DeviceLayer:
         moe_forward(self.desc(T), x, valid, self.router, self.w13, self.w2, self.topk,
                     out, ws, stream)
         return out
+
+    def block_signals(self, T: int) -> torch.Tensor:
+        """Completion counters for forward_signaled: int32 [E+ns, ceil(T/64)]."""
+        return torch.empty((self.E + self.n_shared, (T + 63) // 64), dtype=torch.int32,
+                           device=self.device)
+
+    def forward_signaled(self, x, valid=None, out=None, workspace=None, block_signal=None,
+                         stream=None, consumer_stream=None):
+        """forward with per-(expert, 64-row block) completion counters and the
+        combine waiting on them on consumer_stream.  Returns (out, block_signal)."""
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        ws = workspace if workspace is not None else self.workspace(T)
+        sig = block_signal if block_signal is not None else self.block_signals(T)
+        moe_forward_signaled(self.desc(T), x, valid, self.router, self.w13, self.w2, self.topk,
+                             out, ws, sig, stream, consumer_stream)
+        return out, sig
 
     def route(self, x, valid=None, logits=False, stream=None):
         T = x.shape[0]

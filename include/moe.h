@@ -165,6 +165,56 @@ int moe_forward(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
                 int32_t topk, void* out, void* workspace,
                 size_t workspace_bytes, moe_stream_t stream);
 
+/* Number of int32 completion counters moe_forward_signaled takes:
+ * (E + n_shared) * ceil(T / 64).  Host, pure; 0 for a NULL or malformed desc. */
+size_t moe_block_signal_count(const moe_desc* desc);
+
+/* moe_forward with per-(expert, 64-row block) completion signals and the
+ * combine as their consumer on a second stream ("[SGLang] Single Batch
+ * Overlap for MoE models", combine-signal section: the down-projection GEMM
+ * marks each finished block so that the combine can start on it instead of
+ * waiting for the whole GEMM).
+ *   block_signal    [E + n_shared][ceil(T / 64)] int32, device, caller-owned,
+ *                   moe_block_signal_count(desc) entries.  The call zeroes it
+ *                   on `stream`; each down-projection block then adds, after
+ *                   a release at agent scope, the number of output columns it
+ *                   stored for the 64-row blocks of the expert's segment of
+ *                   the sorted row list (rows 64 b .. 64 b + 63 of expert e:
+ *                   entry [e][b]) that its rows cover.  A block is complete
+ *                   when its entry reaches H; entries of blocks past an
+ *                   expert's rows stay 0.  Once the call has completed every
+ *                   block that holds rows reads exactly H.
+ *   consumer_stream the stream the waiting combine runs on (may equal
+ *                   `stream`).  It waits (an event) for the gate/up GEMM,
+ *                   then combines each token row as soon as the blocks that
+ *                   hold its expert rows are complete; `stream` then waits
+ *                   for it (an event) and combines the rows, if any, that it
+ *                   left because a wait ran past its time bound
+ *                   (moe_set_signal_wait_us; 10 ms by default).  The call
+ *                   returns with all work enqueued; `out` is complete when
+ *                   `stream` reaches that point, and the bits equal
+ *                   moe_forward's (same kernels, same summation order),
+ *                   except that decode-sized calls do not take moe_forward's
+ *                   one-launch down + combine (their y rows go through
+ *                   memory as in larger calls).
+ * Errors as moe_forward, plus MOE_ERR_INVALID_ARG for a NULL block_signal and
+ * MOE_ERR_UNSUPPORTED for fp32 layers.  Two events are created and released
+ * per call; nothing is allocated in device memory.  Calls must not share a
+ * block_signal array or a workspace while either runs. */
+int moe_forward_signaled(const moe_desc* desc, const void* x, const uint8_t* valid_rows,
+                         const void* router_w, const void* w13, const void* w2,
+                         int32_t topk, void* out, void* workspace,
+                         size_t workspace_bytes, int32_t* block_signal,
+                         moe_stream_t stream, moe_stream_t consumer_stream);
+
+/* Time bound of each wait of moe_forward_signaled's waiting combine, in
+ * microseconds (0 .. 1000000; default 10000).  Host, process-wide, read when
+ * a call is enqueued.  With 0 a wait gives up at once unless its blocks are
+ * already complete, which sends the rows to the rest pass on `stream` (tests
+ * use it to exercise that pass; the output bits do not change).
+ * MOE_ERR_INVALID_ARG outside the range. */
+int moe_set_signal_wait_us(int32_t us);
+
 /* Bytes of the fixed device scratch that moe_forward_noalloc works in. */
 #define MOE_SCRATCH_BYTES (64u << 20)
 

@@ -43,6 +43,13 @@ int main(void) {
   check(moe_forward(&d, NULL, NULL, NULL, NULL, NULL, 3, NULL, NULL, ws, NULL) ==
             MOE_ERR_INVALID_ARG,
         "moe_forward rejects null buffers");
+  check(moe_forward_signaled(&d, NULL, NULL, NULL, NULL, NULL, 3, NULL, NULL, ws, NULL, NULL,
+                             NULL) == MOE_ERR_INVALID_ARG,
+        "moe_forward_signaled rejects null buffers");
+  check(moe_block_signal_count(&d) == (size_t)48 * 4, "completion counter count");
+  check(moe_block_signal_count(NULL) == 0, "counter count of a null descriptor is 0");
+  check(moe_set_signal_wait_us(-1) == MOE_ERR_INVALID_ARG, "bad wait bound");
+  check(moe_set_signal_wait_us(10000) == MOE_OK, "default wait bound");
   check(moe_set_path_thresholds(-1, -1) == MOE_ERR_INVALID_ARG, "bad path thresholds");
   check(moe_set_fp8_mfma(2) == MOE_ERR_INVALID_ARG, "bad fp8 MFMA switch");
 

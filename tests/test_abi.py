@@ -176,7 +176,8 @@ def test_workspace_grows_with_batch():
 
 def test_profile_hooks_without_records():
     assert moe.stage_names() == ["route_logits", "route_topk", "align", "pack_x", "gate_up",
-                                 "gate_up_gemm", "down", "down_gemm", "combine", "x_split"]
+                                 "gate_up_gemm", "down", "down_gemm", "combine", "x_split",
+                                 "combine_wait"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())
 
@@ -195,6 +196,40 @@ def test_noalloc_validation_before_any_launch():
     big = _d(T=8192)
     assert lib.moe_workspace_size(ctypes.byref(big), 3) > moe.SCRATCH_BYTES
     assert F(big) == -3
+
+
+def test_signaled_validation_before_any_launch():
+    """moe_forward_signaled: bad descriptors, null pointers (the counters
+    included), fp32 layers and short workspaces are rejected before any
+    launch; the counter count is (E + n_shared) ceil(T / 64)."""
+    lib = moe.load_library()
+    d = _d()
+    big = lib.moe_workspace_size(ctypes.byref(d), 3)
+    S = lambda desc, sig=FAKE, ws_bytes=big, x=FAKE, k=3: lib.moe_forward_signaled(
+        ctypes.byref(desc) if desc is not None else None, x, None, FAKE, FAKE, FAKE, k, FAKE,
+        FAKE, ws_bytes, sig, None, None)
+    assert S(None) == -1
+    assert S(_d(T=0)) == -1
+    assert S(d, sig=None) == -1
+    assert S(d, x=None) == -1
+    assert S(d, k=0) == -1
+    assert S(d, ws_bytes=big - 1) == -3
+    f32 = _d(H=256, I=64, act_dtype=moe.MOE_F32, w_dtype=moe.MOE_F32)
+    assert S(f32, ws_bytes=lib.moe_workspace_size(ctypes.byref(f32), 3)) == -2
+    C = lambda desc: lib.moe_block_signal_count(ctypes.byref(desc) if desc else None)
+    assert C(None) == 0
+    assert C(_d(T=1, E=48)) == 48
+    assert C(_d(T=64, E=48)) == 48
+    assert C(_d(T=65, E=48, n_shared=1)) == 2 * 49
+    assert C(_d(T=8192, E=256)) == 256 * 128
+
+
+def test_signal_wait_bound_validation():
+    lib = moe.load_library()
+    assert lib.moe_set_signal_wait_us(-1) == -1
+    assert lib.moe_set_signal_wait_us(1000001) == -1
+    assert lib.moe_set_signal_wait_us(0) == 0
+    assert lib.moe_set_signal_wait_us(10000) == 0
 
 
 def test_scratch_bytes_matches_header():
