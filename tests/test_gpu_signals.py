@@ -115,6 +115,24 @@ def test_signaled_small_layers_match_oracle(kw):
     assert np.array_equal(sig.cpu().numpy(), _expected_signals(layer, ids, vd, xd.shape[0]))
 
 
+@pytest.mark.parametrize("block_m", [64, 256])
+def test_signaled_block_m_is_forward_bitwise(block_m):
+    """Larger segment padding in the sorted list moves the segment starts;
+    the counters index blocks from each segment's start either way."""
+    kw = dict(T=1300, H=256, E=8, k=2, I=128, n_shared=1, valid_frac=0.8)
+    inp = random_small(seed=157, **kw)
+    log(f"[case] signaled block_m={block_m}: {kw}")
+    layer = device_layer(inp, packed=True, block_m=block_m)
+    xd = inp.x.cuda()
+    vd = inp.valid.cuda()
+    with gemm_path():
+        ref = layer.forward(xd, vd)
+        torch.cuda.synchronize()
+        out, sig, ids = _run_signaled(layer, xd, vd)
+    assert torch.equal(out, ref)
+    assert np.array_equal(sig.cpu().numpy(), _expected_signals(layer, ids, vd, xd.shape[0]))
+
+
 def test_signaled_on_one_stream():
     """consumer_stream = stream: the waits find every block complete."""
     kw = dict(T=1300, H=256, E=8, k=2, I=128, n_shared=1)
