@@ -12,16 +12,18 @@ every other workload with its own step count and nests the results under
 mixed-phase gather, the 8192-row prefill micro-batch with fp8 weights (the
 MFMA-bound half of the metric), the two micro-batches on two HIP streams,
 the unsplit 16384-row batch and the request-boundary split (7003 / 9381),
-the tiny fp32 correctness layer, and the gather and the prefill micro-batch
+the tiny fp32 correctness layer, the gather and the prefill micro-batch
 through moe_forward_signaled (per-(expert, 64-row block) completion counters
-from the down kernels, the combine consuming them on a second stream).
+from the down kernels, the combine consuming them on a second stream), and
+the two decode workloads with the gate/up and the down in one launch.
 Prints one JSON line.
 
 Other modes (profiling runs; the default run takes none of them):
   --config NAME       only that workload (tiny, decode_e48, decode_e256_shared,
                       gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8,
                       prefill_unsplit, prefill_boundary_split,
-                      gather_padded_e48_signaled, prefill_ub_fp8_signaled)
+                      gather_padded_e48_signaled, prefill_ub_fp8_signaled,
+                      decode_e48_one_launch, decode_e256_shared_one_launch)
   --no-cpu-baseline   skip the oracle timing
   --copy-calibrate    time a plain 1 GiB device copy (for counter scaling)
 """
@@ -49,11 +51,14 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 HEADLINE = "decode_e48"
 NESTED = ["decode_e256_shared", "gather_padded_e48", "prefill_ub_fp8", "prefill_pair_fp8",
           "prefill_unsplit", "prefill_boundary_split", "tiny",
-          "gather_padded_e48_signaled", "prefill_ub_fp8_signaled"]
+          "gather_padded_e48_signaled", "prefill_ub_fp8_signaled",
+          "decode_e48_one_launch", "decode_e256_shared_one_launch"]
 # workloads run through moe_forward_signaled: the down kernels raise
 # per-(expert, 64-row block) completion counters and the combine consumes
 # them on a second stream
 SIGNALED = "_signaled"
+# workloads run with the gate/up and down in one launch (moe_set_one_launch)
+ONE_LAUNCH = "_one_launch"
 # two-call variants of the prefill workload: (first rows, second rows)
 PREFILL_SPLITS = {"prefill_pair_fp8": "midpoint", "prefill_boundary_split": "boundary"}
 
@@ -214,7 +219,9 @@ class Workload:
 
         self.name = name
         self.signaled = name.endswith(SIGNALED)
+        self.one_launch = name.endswith(ONE_LAUNCH)
         bname = name[:-len(SIGNALED)] if self.signaled else name
+        bname = bname[:-len(ONE_LAUNCH)] if self.one_launch else bname
         self.split = PREFILL_SPLITS.get(bname)
         whole = bname in ("prefill_unsplit",) or self.split is not None
         base = get_config("prefill_ub_fp8" if whole else bname)
@@ -254,6 +261,13 @@ class Workload:
             if self.signaled:
                 self.layer.forward_signaled(self.x, self.valid, self.out, self.ws, self.sig,
                                             consumer_stream=self.consumer)
+            elif self.one_launch:
+                import expert_layer_moe_amd as moe
+                moe.moe_set_one_launch(True)
+                try:
+                    self.layer.forward(self.x, self.valid, self.out, self.ws)
+                finally:
+                    moe.moe_set_one_launch(False)
             else:
                 self.layer.forward(self.x, self.valid, self.out, self.ws)
             return
@@ -326,6 +340,8 @@ def config_of(wl):
            "two_streams": wl.parts is not None}
     if wl.signaled:
         cfg["block_signals"] = True
+    if wl.one_launch:
+        cfg["one_launch_gate_up_down"] = True
     if wl.parts is not None:
         cfg["calls_rows"] = list(wl.rows)
     return cfg
@@ -357,7 +373,10 @@ def measure_nested(name, steps, warmup):
            "steps": steps, "warmup": warmup, "dtype": compute_dtype(wl.cfg),
            "config": config_of(wl)}
     rec["step"] = step_fractions(wl, ms)
-    if wl.parts is None and wl.cfg.act != "f32":
+    if wl.one_launch:
+        # gate/up and down share one kernel: no gate/up kernel of its own
+        rec["stages_us"] = stage_breakdown(wl, steps)
+    elif wl.parts is None and wl.cfg.act != "f32":
         dom = dominant_kernel(wl)
         moe.moe_profile_enable([dom])
         for _ in range(steps):
@@ -383,7 +402,8 @@ def run_headline(args, name):
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
-    dom = dominant_kernel(wl) if wl.parts is None and wl.cfg.act != "f32" else None
+    dom = (dominant_kernel(wl)
+           if wl.parts is None and wl.cfg.act != "f32" and not wl.one_launch else None)
 
     # timed region: K steps; on the launch stream, a HIP event pair brackets
     # the dominant kernel's launch (and nothing else) in every EVERY-th step,

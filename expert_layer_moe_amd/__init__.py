@@ -4,7 +4,7 @@ from .binding import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_LAYOUT_FRAG16,
                       MOE_LAYOUT_ROW_MAJOR, MoeError, alloc_workspace,
                       load_library, make_desc, moe_align, moe_desc, moe_forward,
                       moe_forward_noalloc, moe_forward_signaled, moe_block_signal_count,
-                      moe_set_signal_wait_us, SCRATCH_BYTES,
+                      moe_set_signal_wait_us, moe_set_one_launch, SCRATCH_BYTES,
                       moe_pack_weights, moe_set_fp8_mfma, moe_set_path_thresholds,
                       moe_profile_enable, moe_profile_read, moe_route,
                       moe_status_str, moe_workspace_size, stage_names)
@@ -14,7 +14,7 @@ __all__ = [
     "MOE_BF16", "MOE_F32", "MOE_FP8_E4M3", "MOE_LAYOUT_FRAG16", "MOE_LAYOUT_ROW_MAJOR",
     "MoeError", "alloc_workspace", "load_library", "make_desc", "moe_align", "moe_desc",
     "moe_forward", "moe_forward_noalloc", "moe_forward_signaled", "moe_block_signal_count",
-    "moe_set_signal_wait_us", "SCRATCH_BYTES", "moe_pack_weights", "moe_set_fp8_mfma", "moe_set_path_thresholds",
+    "moe_set_signal_wait_us", "moe_set_one_launch", "SCRATCH_BYTES", "moe_pack_weights", "moe_set_fp8_mfma", "moe_set_path_thresholds",
     "moe_profile_enable", "moe_profile_read", "moe_route", "moe_status_str",
     "moe_workspace_size", "stage_names", "DeviceLayer",
 ]

@@ -22,7 +22,7 @@ _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
 
 EXPORTS = ["moe_workspace_size", "moe_route", "moe_align", "moe_forward",
-           "moe_forward_noalloc", "moe_forward_signaled", "moe_block_signal_count", "moe_set_signal_wait_us",
+           "moe_forward_noalloc", "moe_forward_signaled", "moe_block_signal_count", "moe_set_signal_wait_us", "moe_set_one_launch",
            "moe_pack_weights", "moe_set_path_thresholds", "moe_set_fp8_mfma", "moe_status_str", "moe_num_stages", "moe_stage_name",
            "moe_profile_enable", "moe_profile_read"]
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_block_signal_count.restype = SZ
     lib.moe_set_signal_wait_us.argtypes = [I32]
     lib.moe_set_signal_wait_us.restype = ctypes.c_int
+    lib.moe_set_one_launch.argtypes = [I32]
+    lib.moe_set_one_launch.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [D, P, P, P, P, P]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.moe_set_fp8_mfma.argtypes = [I32]
@@ -238,6 +240,12 @@ def moe_forward_signaled(desc, x, valid_rows, router_w, w13, w2, topk, out, work
 def moe_set_signal_wait_us(us: int = 10000):
     """Time bound of each wait of the signaled combine (process-wide)."""
     _check(load_library().moe_set_signal_wait_us(us))
+
+
+def moe_set_one_launch(enable: bool = False):
+    """Calls where every segment streams: gate/up and down in one launch
+    (True) or two (False, the default).  Process-wide."""
+    _check(load_library().moe_set_one_launch(1 if enable else 0))
 
 
 SCRATCH_BYTES = 64 << 20   # MOE_SCRATCH_BYTES

@@ -14,6 +14,7 @@
 #include "moe_common.h"
 #include "moe_kernels.h"
 
+#include <algorithm>
 #include <climits>
 #include <type_traits>
 
@@ -47,10 +48,10 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // n_items(seg) x n_cols units, ordered column-group major: the items of a
 // segment that read the same weight columns are neighbours in dispatch
 // order (same XCD, at the same time), which lets them share those weights
-// through L2.
+// through L2.  With item non-null, *item = the unit's item in the table.
 __device__ __forceinline__ int unit_of_segment(int u, int n_cols, const int32_t* item_seg,
                                                const int32_t* item_row0, const int32_t* seg_cnt,
-                                               int& cg, int& it) {
+                                               int& cg, int& it, int* item = nullptr) {
   const int ig = u / n_cols;   // an item of the unit's segment
   const int e = item_seg[ig];
   const int ni = (seg_cnt[e] + kStreamItemRows - 1) / kStreamItemRows;
@@ -58,6 +59,7 @@ __device__ __forceinline__ int unit_of_segment(int u, int n_cols, const int32_t*
   const int local = u - i0 * n_cols;
   cg = local / ni;
   it = local - cg * ni;
+  if (item != nullptr) *item = i0 + it;
   return e;
 }
 
@@ -100,6 +102,217 @@ __device__ __forceinline__ int round_unit(int u0, int n_live) {
 // measured faster than packing it (decode_e48 step 0.265 -> 0.255 ms,
 // decode_e256_shared 0.500 -> 0.475 ms); with many rows per segment
 // (gather_padded_e48) the copy is faster (gate/up 241 against 288 us).
+// One unit (work item lid of the item table, column group) of the streaming
+// gate/up; returns the index of the unit's item in the item table.  Called
+// by every thread of a 256-thread block (the K-part sums meet in red).
+template <int KS, int MT, int KU, int CGN, bool FP8, bool PW, bool XD>
+__device__ __forceinline__ int gate_up_unit(
+    int lid, const uint16_t* __restrict__ xp, const void* __restrict__ w13,
+    const float* __restrict__ s13, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
+    const int32_t* __restrict__ item_row0, uint16_t* __restrict__ h, int H, int I, int n_cg,
+    const int32_t* __restrict__ sorted_ids, int topk,
+    floatx4 (&red)[KS > 1 ? 4 : 1][2][MT][kWave]) {
+  static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
+  constexpr int CGW = 4 / KS;   // waves side by side along the columns
+  int cgb, it, item;
+  const int e = unit_of_segment(lid, n_cg, item_seg, item_row0, seg_cnt, cgb, it, &item);
+  const int cnt = seg_cnt[e];
+  const int row0 = seg_off[e];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int ks = wave % KS, cw = wave / KS;
+  const int m = lane % 16, g = lane / 16;
+  const int klen = H / KS, kbeg = ks * klen;
+  // the wave's column tiles j: columns c0[j] .. + 15 (a tile past I is
+  // neither loaded nor stored)
+  bool col_ok[CGN];
+  int c0[CGN];
+  // this lane's element offsets in the gate / up rows at step 0 of its K
+  // part, and the distance of one MFMA K step (row-major: 32 elements along
+  // the row; fragment-packed: the next 512-element block of the same tile)
+  constexpr size_t wstep = PW ? 512 : 32;
+  size_t wg_off[CGN], wu_off[CGN];
+  const float* sg[CGN];
+  const float* su[CGN];
+#pragma unroll
+  for (int j = 0; j < CGN; ++j) {
+    const int c = ((cgb * CGW + cw) * CGN + j) * 16;
+    col_ok[j] = c < I;
+    c0[j] = col_ok[j] ? c : 0;
+    if constexpr (PW) {
+      const size_t tg = ((size_t)e * 2 * I + c0[j]) / 16, tu = tg + I / 16;
+      wg_off[j] = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+      wu_off[j] = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
+    } else {
+      wg_off[j] = ((size_t)e * 2 * I + c0[j] + m) * H + kbeg + 8 * g;
+      wu_off[j] = wg_off[j] + (size_t)I * H;
+    }
+    sg[j] = su[j] = nullptr;
+    if constexpr (FP8) {
+      const int nkb = H / 128;
+      sg[j] = s13 + ((size_t)e * (2 * I / 128) + c0[j] / 128) * nkb;
+      su[j] = s13 + ((size_t)e * (2 * I / 128) + (I + c0[j]) / 128) * nkb;
+    }
+  }
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // the item's 16-row tiles [tb, te) of the segment
+  const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
+  for (int t0 = tb; t0 < te; t0 += MT) {
+    // this lane's token row of each tile at the start of its K part:
+    // fragment-ordered tiles of xp (row0 is a multiple of 16; step s of
+    // tile t at xa + 512 s), or row m of the tile straight from x (XD;
+    // step s at xa + 32 s; a padding row reads any row: the MFMA keeps rows
+    // apart and its results are never stored)
+    const uint16_t* xa[MT];
+    constexpr size_t xstep = XD ? 32 : 512;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (XD) {
+        const int sid = t0 + mt < te ? sorted_ids[row0 + (t0 + mt) * 16 + m] : -1;
+        xa[mt] = xp + (size_t)(sid >= 0 ? sid / topk : 0) * H + kbeg + 8 * g;
+      } else {
+        xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
+      }
+    }
+    floatx4 ag[CGN][MT], au[CGN][MT];
+#pragma unroll
+    for (int j = 0; j < CGN; ++j)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        ag[j][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        au[j][mt] = ag[j][mt];
+      }
+    // W13 of a segment with one item is read by this block alone:
+    // non-temporal loads (measured faster on the decode batches); the items
+    // of a larger segment share it through L2 (normal loads measured faster)
+    auto k_loop = [&](auto nt_tag) {
+      constexpr bool kNT = decltype(nt_tag)::value;
+      // The blocks of one item read the same token rows; started at the
+      // same K they would all ask the same L2 lines at once.  Where those
+      // rows come straight from x (XD), each group of 32 columns starts
+      // its K loop at its own batch (a fixed order per column, so the sums
+      // do not depend on the block shape): decode_e48 gate/up 157 -> 149
+      // us.  From the packed copy, asking at once is what lets the L2
+      // serve them once: without the rotation gather_padded_e48's gate/up
+      // fetches 1036 instead of 1263 MB, in the same time.
+      const int nbat = klen / (32 * KU);
+      const int rot = XD ? (c0[0] / 32) % nbat * (32 * KU) : 0;
+      for (int kk0 = 0; kk0 < klen; kk0 += 32 * KU) {
+        const int kk = kk0 + rot < klen ? kk0 + rot : kk0 + rot - klen;
+        bf16x8 bg[KU][CGN], bu[KU][CGN], a[KU][MT];
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int j = 0; j < CGN; ++j) {
+            if (j == 0 || col_ok[j]) {
+              bg[u][j] = load_w8<FP8, kNT>(w13, wg_off[j] + (size_t)(kk / 32 + u) * wstep);
+              bu[u][j] = load_w8<FP8, kNT>(w13, wu_off[j] + (size_t)(kk / 32 + u) * wstep);
+            } else {
+              bg[u][j] = bu[u][j] = as_bf16x8(zero);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < KU; ++u)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * xstep) : zero);
+        if constexpr (FP8) {
+#pragma unroll
+          for (int j = 0; j < CGN; ++j) {
+            floatx4 pg[MT], pu[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+              pu[mt] = pg[mt];
+            }
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te) {
+                  pg[mt] = mfma16x16x32(a[u][mt], bg[u][j], pg[mt]);
+                  pu[mt] = mfma16x16x32(a[u][mt], bu[u][j], pu[mt]);
+                }
+            const int kb = (kbeg + kk) >> 7;
+            const float scg = sg[j][kb], scu = su[j][kb];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                ag[j][mt][i] = fmaf(scg, pg[mt][i], ag[j][mt][i]);
+                au[j][mt][i] = fmaf(scu, pu[mt][i], au[j][mt][i]);
+              }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (t0 + mt < te)
+#pragma unroll
+                for (int j = 0; j < CGN; ++j) {
+                  ag[j][mt] = mfma16x16x32(a[u][mt], bg[u][j], ag[j][mt]);
+                  au[j][mt] = mfma16x16x32(a[u][mt], bu[u][j], au[j][mt]);
+                }
+        }
+      }
+    };
+    // (fragment-packed weights only, as for W2 in the down kernel)
+    if (col_ok[0]) {
+      if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
+    }
+#pragma unroll
+    for (int j = 0; j < CGN; ++j) {
+      if constexpr (KS == 1) {
+        if (col_ok[j]) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = (t0 + mt) * 16 + 4 * g + i;
+              if (r < cnt)
+                h[frag_index(row0 + r, c0[j] + m, I)] =
+                    f32_to_bf16_bits(silu_mul(ag[j][mt][i], au[j][mt][i]));
+            }
+        }
+      } else {
+        // column tile j of every wave through the one LDS buffer
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          red[wave][0][mt][lane] = ag[j][mt];
+          red[wave][1][mt][lane] = au[j][mt];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          if ((mt % KS) == ks && t0 + mt < te && col_ok[j]) {
+            floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
+#pragma unroll
+            for (int q = 1; q < KS; ++q) {
+              const floatx4 g2 = red[cw * KS + q][0][mt][lane];
+              const floatx4 u2 = red[cw * KS + q][1][mt][lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                G[i] += g2[i];
+                U[i] += u2[i];
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = (t0 + mt) * 16 + 4 * g + i;
+              if (r < cnt) h[frag_index(row0 + r, c0[j] + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  return item;
+}
+
+// The streaming gate/up launch: a capped grid looping over the units.
 template <int KS, int MT, int KU, int CGN, bool FP8, bool PW, bool XD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FP8 || CGN > 1 ? 2 : 3)))
 void gate_up_stream_kernel(
@@ -110,206 +323,13 @@ void gate_up_stream_kernel(
     uint16_t* __restrict__ h, int H, int I, int max_items, int n_cg,
     const int32_t* __restrict__ sorted_ids, int topk) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
-  constexpr int CGW = 4 / KS;   // waves side by side along the columns
   __shared__ floatx4 red[KS > 1 ? 4 : 1][2][MT][kWave];
   const int n_live = min(*n_items, max_items) * n_cg;
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
     const int lid = round_unit(u0, n_live);
     if (lid < 0) continue;
-    int cgb, it;
-    const int e = unit_of_segment(lid, n_cg, item_seg, item_row0, seg_cnt, cgb, it);
-    const int cnt = seg_cnt[e];
-    const int row0 = seg_off[e];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int ks = wave % KS, cw = wave / KS;
-    const int m = lane % 16, g = lane / 16;
-    const int klen = H / KS, kbeg = ks * klen;
-    // the wave's column tiles j: columns c0[j] .. + 15 (a tile past I is
-    // neither loaded nor stored)
-    bool col_ok[CGN];
-    int c0[CGN];
-    // this lane's element offsets in the gate / up rows at step 0 of its K
-    // part, and the distance of one MFMA K step (row-major: 32 elements along
-    // the row; fragment-packed: the next 512-element block of the same tile)
-    constexpr size_t wstep = PW ? 512 : 32;
-    size_t wg_off[CGN], wu_off[CGN];
-    const float* sg[CGN];
-    const float* su[CGN];
-#pragma unroll
-    for (int j = 0; j < CGN; ++j) {
-      const int c = ((cgb * CGW + cw) * CGN + j) * 16;
-      col_ok[j] = c < I;
-      c0[j] = col_ok[j] ? c : 0;
-      if constexpr (PW) {
-        const size_t tg = ((size_t)e * 2 * I + c0[j]) / 16, tu = tg + I / 16;
-        wg_off[j] = (tg * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-        wu_off[j] = (tu * (H / 32) + kbeg / 32) * 512 + 8 * lane;
-      } else {
-        wg_off[j] = ((size_t)e * 2 * I + c0[j] + m) * H + kbeg + 8 * g;
-        wu_off[j] = wg_off[j] + (size_t)I * H;
-      }
-      sg[j] = su[j] = nullptr;
-      if constexpr (FP8) {
-        const int nkb = H / 128;
-        sg[j] = s13 + ((size_t)e * (2 * I / 128) + c0[j] / 128) * nkb;
-        su[j] = s13 + ((size_t)e * (2 * I / 128) + (I + c0[j]) / 128) * nkb;
-      }
-    }
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    // the item's 16-row tiles [tb, te) of the segment
-    const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
-    for (int t0 = tb; t0 < te; t0 += MT) {
-      // this lane's token row of each tile at the start of its K part:
-      // fragment-ordered tiles of xp (row0 is a multiple of 16; step s of
-      // tile t at xa + 512 s), or row m of the tile straight from x (XD;
-      // step s at xa + 32 s; a padding row reads any row: the MFMA keeps rows
-      // apart and its results are never stored)
-      const uint16_t* xa[MT];
-      constexpr size_t xstep = XD ? 32 : 512;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        if constexpr (XD) {
-          const int sid = t0 + mt < te ? sorted_ids[row0 + (t0 + mt) * 16 + m] : -1;
-          xa[mt] = xp + (size_t)(sid >= 0 ? sid / topk : 0) * H + kbeg + 8 * g;
-        } else {
-          xa[mt] = xp + ((size_t)(row0 >> 4) + t0 + mt) * 16 * H + (size_t)(kbeg / 32) * 512 + 8 * lane;
-        }
-      }
-      floatx4 ag[CGN][MT], au[CGN][MT];
-#pragma unroll
-      for (int j = 0; j < CGN; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          ag[j][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-          au[j][mt] = ag[j][mt];
-        }
-      // W13 of a segment with one item is read by this block alone:
-      // non-temporal loads (measured faster on the decode batches); the items
-      // of a larger segment share it through L2 (normal loads measured faster)
-      auto k_loop = [&](auto nt_tag) {
-        constexpr bool kNT = decltype(nt_tag)::value;
-        // The blocks of one item read the same token rows; started at the
-        // same K they would all ask the same L2 lines at once.  Where those
-        // rows come straight from x (XD), each group of 32 columns starts
-        // its K loop at its own batch (a fixed order per column, so the sums
-        // do not depend on the block shape): decode_e48 gate/up 157 -> 149
-        // us.  From the packed copy, asking at once is what lets the L2
-        // serve them once: without the rotation gather_padded_e48's gate/up
-        // fetches 1036 instead of 1263 MB, in the same time.
-        const int nbat = klen / (32 * KU);
-        const int rot = XD ? (c0[0] / 32) % nbat * (32 * KU) : 0;
-        for (int kk0 = 0; kk0 < klen; kk0 += 32 * KU) {
-          const int kk = kk0 + rot < klen ? kk0 + rot : kk0 + rot - klen;
-          bf16x8 bg[KU][CGN], bu[KU][CGN], a[KU][MT];
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int j = 0; j < CGN; ++j) {
-              if (j == 0 || col_ok[j]) {
-                bg[u][j] = load_w8<FP8, kNT>(w13, wg_off[j] + (size_t)(kk / 32 + u) * wstep);
-                bu[u][j] = load_w8<FP8, kNT>(w13, wu_off[j] + (size_t)(kk / 32 + u) * wstep);
-              } else {
-                bg[u][j] = bu[u][j] = as_bf16x8(zero);
-              }
-            }
-#pragma unroll
-          for (int u = 0; u < KU; ++u)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(xa[mt] + (size_t)(kk / 32 + u) * xstep) : zero);
-          if constexpr (FP8) {
-#pragma unroll
-            for (int j = 0; j < CGN; ++j) {
-              floatx4 pg[MT], pu[MT];
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt) {
-                pg[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-                pu[mt] = pg[mt];
-              }
-#pragma unroll
-              for (int u = 0; u < KU; ++u)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                  if (t0 + mt < te) {
-                    pg[mt] = mfma16x16x32(a[u][mt], bg[u][j], pg[mt]);
-                    pu[mt] = mfma16x16x32(a[u][mt], bu[u][j], pu[mt]);
-                  }
-              const int kb = (kbeg + kk) >> 7;
-              const float scg = sg[j][kb], scu = su[j][kb];
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  ag[j][mt][i] = fmaf(scg, pg[mt][i], ag[j][mt][i]);
-                  au[j][mt][i] = fmaf(scu, pu[mt][i], au[j][mt][i]);
-                }
-            }
-          } else {
-#pragma unroll
-            for (int u = 0; u < KU; ++u)
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                if (t0 + mt < te)
-#pragma unroll
-                  for (int j = 0; j < CGN; ++j) {
-                    ag[j][mt] = mfma16x16x32(a[u][mt], bg[u][j], ag[j][mt]);
-                    au[j][mt] = mfma16x16x32(a[u][mt], bu[u][j], au[j][mt]);
-                  }
-          }
-        }
-      };
-      // (fragment-packed weights only, as for W2 in the down kernel)
-      if (col_ok[0]) {
-        if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
-        else k_loop(std::false_type{});
-      }
-#pragma unroll
-      for (int j = 0; j < CGN; ++j) {
-        if constexpr (KS == 1) {
-          if (col_ok[j]) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = (t0 + mt) * 16 + 4 * g + i;
-                if (r < cnt)
-                  h[frag_index(row0 + r, c0[j] + m, I)] =
-                      f32_to_bf16_bits(silu_mul(ag[j][mt][i], au[j][mt][i]));
-              }
-          }
-        } else {
-          // column tile j of every wave through the one LDS buffer
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            red[wave][0][mt][lane] = ag[j][mt];
-            red[wave][1][mt][lane] = au[j][mt];
-          }
-          __syncthreads();
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            if ((mt % KS) == ks && t0 + mt < te && col_ok[j]) {
-              floatx4 G = red[cw * KS][0][mt][lane], U = red[cw * KS][1][mt][lane];
-#pragma unroll
-              for (int q = 1; q < KS; ++q) {
-                const floatx4 g2 = red[cw * KS + q][0][mt][lane];
-                const floatx4 u2 = red[cw * KS + q][1][mt][lane];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  G[i] += g2[i];
-                  U[i] += u2[i];
-                }
-              }
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = (t0 + mt) * 16 + 4 * g + i;
-                if (r < cnt) h[frag_index(row0 + r, c0[j] + m, I)] = f32_to_bf16_bits(silu_mul(G[i], U[i]));
-              }
-            }
-          }
-          __syncthreads();
-        }
-      }
-    }
+    gate_up_unit<KS, MT, KU, CGN, FP8, PW, XD>(lid, xp, w13, s13, seg_off, seg_cnt, item_seg,
+                                             item_row0, h, H, I, n_cg, sorted_ids, topk, red);
   }
 }
 
@@ -326,15 +346,148 @@ void gate_up_stream_kernel(
 // Units: (item, column group), n_ng = ceil(H / (64 * NT)) per item (NT = 4).
 // Y24: y rows as 24-bit floats (bf16-weight calls where every segment
 // streams; the writes of y are what the kernel pays most for besides W2).
+// One unit (work item lid of the item table, 256 output columns) of the
+// streaming down projection, signals included; returns the unit's item.
+template <int MT, int NT, int KU, bool FP8, bool PW, bool Y24>
+__device__ __forceinline__ int down_unit(
+    int lid, const uint16_t* __restrict__ h, const void* __restrict__ w2,
+    const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
+    const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
+    const int32_t* __restrict__ item_row0, void* __restrict__ y, int H, int I, int n_ng,
+    BlockSignals bs, floatx4 (&ytile)[4][16][17]) {
+  static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
+  static_assert(NT == 4, "the store pass moves 64-column tiles");
+  int ngb, it, item;
+  const int e = unit_of_segment(lid, n_ng, item_seg, item_row0, seg_cnt, ngb, it, &item);
+  const int cnt = seg_cnt[e];
+  const int row0 = seg_off[e];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int n0 = (ngb * 4 + wave) * NT * 16;
+  // no barriers in a unit (waves go their own way) unless it raises a
+  // completion signal at its end
+  if (n0 < H) {
+    const int m = lane % 16, g = lane / 16;
+    constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
+    size_t wo[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = min(n0 + nt * 16, H - 16);
+      if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
+      else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
+    }
+    const float* sc = nullptr;
+    if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // the item's 16-row tiles [tb, te) of the segment
+    const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
+    for (int t0 = tb; t0 < te; t0 += MT) {
+      // fragment-ordered h tiles (rows past cnt may hold anything: each token
+      // row feeds only its own output column of the MFMA, never stored)
+      const uint16_t* ha[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
+      floatx4 acc[MT][NT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // W2 of a segment with one item is read by this block alone: non-temporal
+      // loads (measured faster); the items of a larger segment share it
+      // through L2 (normal loads measured faster)
+      auto k_loop = [&](auto nt_tag) {
+        constexpr bool kNT = decltype(nt_tag)::value;
+        for (int kk = 0; kk < I; kk += 32 * KU) {
+          bf16x8 b[KU][NT], a[KU][MT];
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+              b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
+#pragma unroll
+          for (int u = 0; u < KU; ++u)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
+          if constexpr (FP8) {
+            floatx4 p[MT][NT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
+            const int kb = kk >> 7;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+              const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
+            }
+          } else {
+#pragma unroll
+            for (int u = 0; u < KU; ++u)
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt)
+                if (t0 + mt < te)
+#pragma unroll
+                  for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
+          }
+        }
+      };
+      // (fragment-packed weights only: a row-major K step reads half of each
+      // 128-byte line, and the next step needs the line again)
+      if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
+      else k_loop(std::false_type{});
+      // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt +
+      // 4 g .. + 3.  Through LDS: lane l then holds row 4 q + l / 16 of the
+      // tile, columns n0 + 4 (l % 16) .. + 3, for q = 0 .. 3.
+      const int lr = lane / 16, lc = lane % 16;
+      const bool col_in = n0 + 4 * lc < H;   // H is a multiple of 16
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (t0 + mt >= te) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ytile[wave][m][4 * nt + g] = acc[mt][nt];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tr = 4 * q + lr;
+          const int r = (t0 + mt) * 16 + tr;
+          const floatx4 v = ytile[wave][tr][lc];
+          if (r < cnt && col_in) {
+            const size_t yi = (size_t)(row0 + r) * H + n0 + 4 * lc;
+            if constexpr (Y24) store_y24(y, yi, v);
+            else store_y4<FP8>(y, yi, v);
+          }
+        }
+      }
+    }
+  }
+  // the unit's rows (one 64-row block of the segment) x its 256 columns
+  if (bs.sig != nullptr)
+    signal_rows_done(bs, e, it * kStreamItemRows, min(kStreamItemRows, cnt - it * kStreamItemRows),
+                     min(256, H - ngb * 256));
+  return item;
+}
+
+// The streaming down launch: a capped grid looping over the units (with
+// only non-null, just the units whose flag is set).
 template <int MT, int NT, int KU, bool FP8, bool PW, bool Y24>
 __global__ __launch_bounds__(256) void down_stream_kernel(
     const uint16_t* __restrict__ h, const void* __restrict__ w2,
     const float* __restrict__ s2, const int32_t* __restrict__ seg_off,
     const int32_t* __restrict__ seg_cnt, const int32_t* __restrict__ item_seg,
     const int32_t* __restrict__ item_row0, const int32_t* __restrict__ n_items,
-    void* __restrict__ y, int H, int I, int max_items, int n_ng, BlockSignals bs) {
+    void* __restrict__ y, int H, int I, int max_items, int n_ng, BlockSignals bs,
+    const int32_t* __restrict__ only) {
   static_assert(MT * 16 == kStreamItemRows, "one work item per pass");
-  static_assert(NT == 4, "the store pass moves 64-column tiles");
   // per wave: one 16-row x 64-column tile of y on its way out (rows padded
   // to 68 floats against bank conflicts); only its own wave touches it
   __shared__ floatx4 ytile[4][16][17];
@@ -342,123 +495,98 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
   for (int u0 = 0; u0 < n_live; u0 += gridDim.x) {
     const int lid = round_unit(u0, n_live);
     if (lid < 0) continue;
-    int ngb, it;
-    const int e = unit_of_segment(lid, n_ng, item_seg, item_row0, seg_cnt, ngb, it);
-    const int cnt = seg_cnt[e];
-    const int row0 = seg_off[e];
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int n0 = (ngb * 4 + wave) * NT * 16;
-    // no barriers in a unit (waves go their own way) unless it raises a
-    // completion signal at its end
-    if (n0 < H) {
-      const int m = lane % 16, g = lane / 16;
-      constexpr size_t wstep = PW ? 512 : 32;   // elements per MFMA K step
-      size_t wo[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int n = min(n0 + nt * 16, H - 16);
-        if constexpr (PW) wo[nt] = (((size_t)e * H + n) / 16 * (I / 32)) * 512 + 8 * lane;
-        else wo[nt] = ((size_t)e * H + n + m) * I + 8 * g;
+    if (only != nullptr && only[lid] == 0) continue;
+    down_unit<MT, NT, KU, FP8, PW, Y24>(lid, h, w2, s2, seg_off, seg_cnt, item_seg, item_row0, y,
+                                        H, I, n_ng, bs, ytile);
+  }
+}
+
+// Gate/up, SiLU*mul and down in one launch ("Step3 Inference Optimization on
+// AMD Instinct MI308X", optimisation list: the MoE one-stage kernel), for
+// calls where every segment streams, bf16 weights.  A block takes tickets
+// from one counter until they run out: the first n_items * n_cg tickets are
+// gate/up units, the next n_items * n_ng down units (the units of the two
+// streaming kernels, run by the same code).  A gate/up unit stores its h columns, releases them
+// at agent scope and counts itself in its item's counter; a down unit waits
+// until its item's counter reaches n_cg, acquires, and runs.  Tickets are
+// handed out in order to blocks that are running, so every gate/up unit a
+// down unit waits for is held by a running block that waits for nothing: the
+// waits end.  They are also bounded in time (the real-time counter); a wait
+// that runs out sets the give-up flag (later waits then skip) and marks its
+// unit, which the streaming down kernel's rest pass then runs.  h stays in
+// the L2s and memory between the halves, as between the two launches.
+template <int MT, int KUG, int KUD, int CGN, bool PW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void expert_mlp_kernel(
+    const uint16_t* __restrict__ x, const void* __restrict__ w13, const void* __restrict__ w2,
+    const int32_t* __restrict__ seg_off, const int32_t* __restrict__ seg_cnt,
+    const int32_t* __restrict__ item_seg, const int32_t* __restrict__ item_row0,
+    const int32_t* __restrict__ n_items, uint16_t* __restrict__ h, void* __restrict__ y, int H,
+    int I, int max_items, int n_cg, int n_ng, const int32_t* __restrict__ sorted_ids, int topk,
+    OneLaunch ol) {
+  constexpr int KS = 4;   // bf16 weights; every segment streams: 24-bit y rows
+  __shared__ floatx4 red[4][2][MT][kWave];
+  __shared__ floatx4 ytile[4][16][17];
+  __shared__ int s_tk, s_ok;
+  const int n_it = min(*n_items, max_items);
+  const int n_gu = n_it * n_cg, n_all = n_gu + n_it * n_ng;
+  // The block's next ticket, the same in every thread.  Thread 0's work of
+  // an iteration stays between two barriers: with the count-in of a gate/up
+  // unit and the next ticket's atomic as one thread-0 stretch across the
+  // loop's back edge, the compiler let lane 0 alone leave an inner loop to
+  // take the ticket while the block's other lanes went back to the ticket
+  // barrier, read the old ticket and ran the same unit again without end.
+  auto next_ticket = [&]() -> int {
+    if (threadIdx.x == 0) s_tk = atomicAdd(ol.ticket, 1);
+    __syncthreads();
+    const int t = __builtin_amdgcn_readfirstlane(s_tk);
+    __syncthreads();
+    return t;
+  };
+  for (int tk = next_ticket(); tk < n_all; tk = next_ticket()) {
+    if (tk < n_gu) {
+      const int item = gate_up_unit<KS, MT, KUG, CGN, false, PW, true>(
+          tk, x, w13, nullptr, seg_off, seg_cnt, item_seg, item_row0, h, H, I, n_cg, sorted_ids, topk,
+          red);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(ol.item_done + item, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      const float* sc = nullptr;
-      if constexpr (FP8) sc = s2 + (size_t)e * (H / 128) * (I / 128);
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      // the item's 16-row tiles [tb, te) of the segment
-      const int tb = it * MT, te = min((cnt + 15) >> 4, tb + MT);
-      for (int t0 = tb; t0 < te; t0 += MT) {
-        // fragment-ordered h tiles (rows past cnt may hold anything: each token
-        // row feeds only its own output column of the MFMA, never stored)
-        const uint16_t* ha[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          ha[mt] = h + ((size_t)(row0 >> 4) + t0 + mt) * 16 * I + 8 * lane;
-        floatx4 acc[MT][NT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        // W2 of a segment with one item is read by this block alone: non-temporal
-        // loads (measured faster); the items of a larger segment share it
-        // through L2 (normal loads measured faster)
-        auto k_loop = [&](auto nt_tag) {
-          constexpr bool kNT = decltype(nt_tag)::value;
-          for (int kk = 0; kk < I; kk += 32 * KU) {
-            bf16x8 b[KU][NT], a[KU][MT];
-#pragma unroll
-            for (int u = 0; u < KU; ++u)
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt)
-                b[u][nt] = load_w8<FP8, kNT>(w2, wo[nt] + (size_t)(kk / 32 + u) * wstep);
-#pragma unroll
-            for (int u = 0; u < KU; ++u)
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-                a[u][mt] = as_bf16x8(t0 + mt < te ? ld16(ha[mt] + (size_t)(kk / 32 + u) * 512) : zero);
-            if constexpr (FP8) {
-              floatx4 p[MT][NT];
-#pragma unroll
-              for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) p[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int u = 0; u < KU; ++u)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                  if (t0 + mt < te)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) p[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], p[mt][nt]);
-              const int kb = kk >> 7;
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) {
-                const float s = sc[((n0 + nt * 16) / 128) * (I / 128) + kb];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                  for (int i = 0; i < 4; ++i) acc[mt][nt][i] = fmaf(s, p[mt][nt][i], acc[mt][nt][i]);
-              }
-            } else {
-#pragma unroll
-              for (int u = 0; u < KU; ++u)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                  if (t0 + mt < te)
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma16x16x32(b[u][nt], a[u][mt], acc[mt][nt]);
-            }
+    } else {
+      const int lid = tk - n_gu;
+      if (threadIdx.x < kWave) {
+        int ngb, it, item;
+        (void)unit_of_segment(lid, n_ng, item_seg, item_row0, seg_cnt, ngb, it, &item);
+        const uint64_t start = __builtin_amdgcn_s_memrealtime();
+        bool ok = true;
+        while (__hip_atomic_load(ol.item_done + item, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+               n_cg) {
+          if (__hip_atomic_load(ol.giveup, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+              __builtin_amdgcn_s_memrealtime() - start > (uint64_t)ol.ticks) {
+            ok = false;
+            break;
           }
-        };
-        // (fragment-packed weights only: a row-major K step reads half of each
-        // 128-byte line, and the next step needs the line again)
-        if (PW && cnt <= kStreamItemRows) k_loop(std::true_type{});
-        else k_loop(std::false_type{});
-        // acc[mt][nt] lane (m, g): row (t0 + mt) 16 + m, columns n0 + 16 nt +
-        // 4 g .. + 3.  Through LDS: lane l then holds row 4 q + l / 16 of the
-        // tile, columns n0 + 4 (l % 16) .. + 3, for q = 0 .. 3.
-        const int lr = lane / 16, lc = lane % 16;
-        const bool col_in = n0 + 4 * lc < H;   // H is a multiple of 16
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          if (t0 + mt >= te) continue;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) ytile[wave][m][4 * nt + g] = acc[mt][nt];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int tr = 4 * q + lr;
-            const int r = (t0 + mt) * 16 + tr;
-            const floatx4 v = ytile[wave][tr][lc];
-            if (r < cnt && col_in) {
-              const size_t yi = (size_t)(row0 + r) * H + n0 + 4 * lc;
-              if constexpr (Y24) store_y24(y, yi, v);
-              else store_y4<FP8>(y, yi, v);
-            }
+          __builtin_amdgcn_s_sleep(8);
+        }
+        ok = __all(ok);
+        if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        if (threadIdx.x == 0) {
+          s_ok = ok ? 1 : 0;
+          if (!ok) {
+            ol.undone[lid] = 1;
+            __hip_atomic_store(ol.giveup, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
+      __syncthreads();
+      if (s_ok)
+        down_unit<MT, 4, KUD, false, PW, true>(lid, h, w2, nullptr, seg_off, seg_cnt, item_seg,
+                                               item_row0, y, H, I, n_ng, BlockSignals{nullptr, 0},
+                                               ytile);
     }
-    // the unit's rows (one 64-row block of the segment) x its 256 columns
-    if (bs.sig != nullptr)
-      signal_rows_done(bs, e, it * kStreamItemRows, min(kStreamItemRows, cnt - it * kStreamItemRows),
-                       min(256, H - ngb * 256));
+    __syncthreads();   // the iteration ends here for every thread
   }
 }
 
@@ -739,13 +867,14 @@ struct DnArgs {
   void* y;
   int H, I, max_items, n_ng;
   BlockSignals bs;
+  const int32_t* only;   // rest pass: just these units
 };
 
 template <int KU, bool FP8, bool PW, bool Y24>
 void launch_dn(const DnArgs& a) {
   hipLaunchKernelGGL((down_stream_kernel<4, 4, KU, FP8, PW, Y24>), a.grid, dim3(256), 0, a.s, a.h, a.w2,
                      a.s2, a.seg_off, a.seg_cnt, a.item_seg, a.item_row0, a.n_items, a.y, a.H,
-                     a.I, a.max_items, a.n_ng, a.bs);
+                     a.I, a.max_items, a.n_ng, a.bs, a.only);
 }
 
 template <bool FP8, bool PW, bool Y24 = false>
@@ -832,14 +961,51 @@ hipError_t launch_down_cols(int wkind, bool packed, const void* h, const void* w
   return hipGetLastError();
 }
 
+bool expert_mlp_fits(int wkind, int H, int I) {
+  return wkind == W_BF16 && H % 512 == 0 && I % 128 == 0;
+}
+
+hipError_t launch_expert_mlp(int wkind, bool packed, const void* x, const void* w13,
+                             const void* w2, const int32_t* seg_off, const int32_t* seg_cnt,
+                             const int32_t* sorted_ids, const int32_t* item_seg,
+                             const int32_t* item_row0, const int32_t* n_items, int max_items,
+                             void* h, void* y, int H, int I, int k, OneLaunch ol,
+                             hipStream_t s) {
+  if (!expert_mlp_fits(wkind, H, I)) return hipErrorInvalidValue;
+  // the streaming gate/up's shape (a K split in 4, batches of 4 K steps:
+  // the same K order, so the same sums); the down's batches of 2 K steps
+  // instead of 4 (the same order of its K steps, so the same sums) keep the
+  // merged kernel free of register spills
+  const int cgn = packed ? kGuCgn : 1;
+  const int n_cg = (I / 16 + cgn - 1) / cgn;
+  const int n_ng = stream_down_groups(H);
+  const long long units = (long long)max_items * (n_cg + n_ng);
+  if (units > INT_MAX - 8) return hipErrorInvalidValue;
+  // enough blocks for every slot of the chip (two per CU); they loop over
+  // the tickets
+  const dim3 grid((unsigned)std::min<long long>(round8((int)std::min<long long>(units, 1 << 20)),
+                                                512));
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+#define MOE_MLP(CG, P)                                                                          \
+  hipLaunchKernelGGL((expert_mlp_kernel<4, 4, 2, CG, P>), grid, dim3(256), 0, s, xb, w13, w2,     \
+                     seg_off, seg_cnt, item_seg, item_row0, n_items, hb, y, H, I, max_items, n_cg, \
+                     n_ng, sorted_ids, k, ol)
+  if (packed) MOE_MLP(kGuCgn, true);
+  else MOE_MLP(1, false);
+#undef MOE_MLP
+  return hipGetLastError();
+}
+
 hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, const float* s2,
                        const int32_t* block_expert, const int32_t* n_post,
                        const int32_t* seg_off, const int32_t* seg_cnt,
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
-                       int bm, int max_rows, bool y24, hipStream_t s, BlockSignals bs) {
+                       int bm, int max_rows, bool y24, hipStream_t s, BlockSignals bs,
+                       const int32_t* only) {
   if (wkind == W_F32) {
-    if (bs.sig != nullptr) return hipErrorInvalidValue;
+    if (bs.sig != nullptr || only != nullptr) return hipErrorInvalidValue;
     hipLaunchKernelGGL(down_f32_kernel, dim3(max_rows), dim3(256), 0, s,
                        static_cast<const float*>(h), static_cast<const float*>(w2),
                        block_expert, n_post, static_cast<float*>(y), H, I, bm);
@@ -847,10 +1013,10 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
   }
   const bool fp8 = wkind == W_FP8;
   const int ku = pick_ku(I);
-  const int n_ng = (H + 255) / 256;
+  const int n_ng = stream_down_groups(H);
   if ((long long)max_items * n_ng > INT_MAX - 8) return hipErrorInvalidValue;
   DnArgs a{dim3(stream_grid(max_items * n_ng)), s, static_cast<const uint16_t*>(h), w2, s2,
-           seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng, bs};
+           seg_off, seg_cnt, item_seg, item_row0, n_items, y, H, I, max_items, n_ng, bs, only};
   if (fp8) {
     if (packed) launch_dn_ku<true, true>(ku, a);
     else launch_dn_ku<true, false>(ku, a);

@@ -31,10 +31,11 @@ struct Plan {
   int max_items;  // bound on the streaming kernels' work items
   size_t off_part, off_ids, off_w, off_sorted, off_bexp, off_offs, off_npost,
       off_slot, off_cnt, off_tseg, off_trow, off_ntiles, off_iseg, off_irow, off_nitems,
-      off_span, off_h, off_y, off_xq, off_sx, off_done, total;
+      off_span, off_h, off_y, off_xq, off_sx, off_done, off_one, total;
   bool xsplit;    // fp8 weights on the GEMM path: token rows as two e4m3 terms
   int yfmt;       // format of the expert output rows y (moe::YFmt)
   bool down_cols; // down projection and combine in one launch (small batches)
+  bool one_launch; // gate/up and down in one launch (moe_set_one_launch)
 };
 
 // Rows per segment above which the tiled GEMM kernels (128-row tiles, weight
@@ -49,6 +50,9 @@ std::atomic<int> g_gemm_min_tiles{-1};   // -1: enough tiles to fill the chip
 // or bf16 MFMA on dequantised weights (0, the default: the same MFMA cycles,
 // measured no faster, and no split pass); moe_set_fp8_mfma
 std::atomic<int> g_fp8_mfma{0};
+// Calls where every segment streams: gate/up and down in one launch (1) or
+// two (0, the default: measured faster); moe_set_one_launch
+std::atomic<int> g_one_launch{0};
 
 // Padding granularity of the expert segments in the sorted row list: every
 // kernel works on 16-row MFMA tiles of a segment (the tiled GEMMs on 128-row
@@ -99,6 +103,12 @@ int done_chunks(int H) { return (H + 1023) / 1024; }
 // ceil(T / 64) blocks.
 size_t signal_count(const moe_desc* d) {
   return (size_t)(d->E + d->n_shared) * (size_t)((d->T + 63) / 64);
+}
+
+// Words of the one-launch gate/up + down's counters and flags: ticket, give-up
+// flag, one spare, then max_items item counts and max_items * n_ng flags.
+size_t one_launch_words(int max_items, int H) {
+  return 3 + (size_t)max_items * (1 + moe::stream_down_groups(H));
 }
 
 // The tiled kernels index x with 32-bit element offsets.
@@ -203,6 +213,13 @@ int make_plan(const moe_desc* d, int32_t topk, Plan* p) {
   // done flags of the waiting combine (moe_forward_signaled): one per (row,
   // column chunk of the combine grid), then the give-up flag
   p->off_done = take(((size_t)p->T * done_chunks(p->H) + 1) * 4);
+  // the one-launch gate/up + down: ticket, give-up flag, per-item counts,
+  // per-down-unit rest flags
+  p->off_one = take(one_launch_words(p->max_items, p->H) * 4);
+  const int wk = p->w == MOE_FP8_E4M3 ? moe::W_FP8 : (p->w == MOE_BF16 ? moe::W_BF16 : moe::W_F32);
+  p->one_launch = g_one_launch.load() != 0 && p->big_thr == INT_MAX && p->act == MOE_BF16 &&
+                  moe::expert_mlp_fits(wk, p->H, p->I);
+  if (p->one_launch) p->down_cols = false;
   p->total = o;
   return MOE_OK;
 }
@@ -215,11 +232,11 @@ T* at(void* ws, size_t off) {
 // ---- measurement hooks -------------------------------------------------------
 enum Stage {
   S_LOGITS = 0, S_TOPK, S_ALIGN, S_PACK_X, S_GATE_UP, S_GATE_UP_GEMM, S_DOWN, S_DOWN_GEMM,
-  S_COMBINE, S_X_SPLIT, S_COMBINE_WAIT, S_COUNT
+  S_COMBINE, S_X_SPLIT, S_COMBINE_WAIT, S_EXPERT_MLP, S_COUNT
 };
 const char* kStageNames[S_COUNT] = {"route_logits", "route_topk", "align", "pack_x", "gate_up",
                                     "gate_up_gemm", "down", "down_gemm", "combine", "x_split",
-                                    "combine_wait"};
+                                    "combine_wait", "expert_mlp"};
 
 struct ProfRecord {
   int stage;
@@ -334,6 +351,35 @@ int forward_impl(const Plan& p, const moe_desc* desc, const void* x, const uint8
                           ntiles, at<int32_t>(ws, p.off_span), iseg, irow, nitems,
                           s) != hipSuccess)
       return MOE_ERR_HIP;
+  }
+  if (p.one_launch) {
+    // gate/up and down in one launch, the down units a wait left in the
+    // streaming down kernel's rest pass, then the combine
+    int32_t* one = at<int32_t>(ws, p.off_one);
+    const moe::OneLaunch ol{one, one + 3, one + 3 + p.max_items, one + 1,
+                            100LL * g_wait_us.load()};
+    if (moe::launch_zero_i32(one, one_launch_words(p.max_items, p.H), nullptr, 0, s) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    {
+      StageTimer tm(S_EXPERT_MLP, s);
+      if (moe::launch_expert_mlp(wkind, packed, x, w13, w2, offs, cnt, sorted, iseg, irow,
+                                 nitems, p.max_items, h, y, p.H, p.I, p.k, ol, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+    {
+      StageTimer tm(S_DOWN, s);
+      if (moe::launch_down(wkind, packed, h, w2, desc->w2_scale, bexp, npost, offs, cnt, iseg,
+                           irow, nitems, p.max_items, y, p.H, p.I, p.bm, p.cap,
+                           p.yfmt == moe::Y_F24, s, moe::BlockSignals{nullptr, 0},
+                           ol.undone) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+    StageTimer tm(S_COMBINE, s);
+    if (moe::launch_combine(y, p.yfmt, ids, wts, slot, p.T, p.H, p.k, p.ns, out,
+                            p.act == MOE_BF16, s) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
   }
   // the streaming gate/up reads the token rows straight from x when every
   // segment streams, else from a fragment-ordered copy of the streaming
@@ -490,6 +536,12 @@ int moe_set_signal_wait_us(int32_t us) {
   return MOE_OK;
 }
 
+int moe_set_one_launch(int32_t enable) {
+  if (enable != 0 && enable != 1) return MOE_ERR_INVALID_ARG;
+  g_one_launch.store(enable);
+  return MOE_OK;
+}
+
 int moe_set_fp8_mfma(int32_t enable) {
   if (enable != 0 && enable != 1) return MOE_ERR_INVALID_ARG;
   g_fp8_mfma.store(enable);
@@ -588,8 +640,9 @@ int moe_forward_signaled(const moe_desc* desc, const void* x, const uint8_t* val
   if (p.w == MOE_F32 || p.act != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
   // the per-assignment y rows are the signals' subject: no one-launch down +
-  // combine
+  // combine, and the down units are those of the streaming down kernel
   p.down_cols = false;
+  p.one_launch = false;
   const SignalCtx sc{block_signal, static_cast<hipStream_t>(consumer_stream)};
   return forward_impl(p, desc, x, valid_rows, router_w, w13, w2, out, workspace,
                       static_cast<hipStream_t>(stream), &sc);

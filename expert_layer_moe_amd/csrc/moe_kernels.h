@@ -34,6 +34,17 @@ struct CombineWait {
   long long ticks;          // time bound of one wait, in 100 MHz real-time ticks
 };
 
+// Gate/up and down of the streaming kernels in one launch (calls where every
+// segment streams; see launch_expert_mlp).  All counters and flags must be
+// zero at the launch.
+struct OneLaunch {
+  int32_t* ticket;      // next unit to take
+  int32_t* item_done;   // [max_items]: gate/up units of each item finished
+  int32_t* undone;      // [max_items * n_ng]: down units left to the rest pass
+  int32_t* giveup;      // set once a wait runs out of time; later waits skip
+  long long ticks;      // time bound of one wait, in 100 MHz real-time ticks
+};
+
 // ---- route -----------------------------------------------------------------
 // Partial router logits: part[z][t][e] = sum over the z-th K chunk of
 // x[t,:] * R[e,:].  bf16 inputs use MFMA; fp32 inputs use a plain FMA loop
@@ -153,7 +164,23 @@ hipError_t launch_down(int wkind, bool packed, const void* h, const void* w2, co
                        const int32_t* item_seg, const int32_t* item_row0,
                        const int32_t* n_items, int max_items, void* y, int H, int I,
                        int bm, int max_rows, bool y24, hipStream_t s,
-                       BlockSignals bs = BlockSignals{nullptr, 0});
+                       BlockSignals bs = BlockSignals{nullptr, 0},
+                       const int32_t* only = nullptr);
+// Output column groups per item of the streaming down kernel (its units per
+// item).
+inline int stream_down_groups(int H) { return (H + 255) / 256; }
+// Calls where every segment streams: gate/up (token rows straight from x)
+// and down in one launch, y rows as launch_down writes them (24-bit); down
+// units whose wait ran out are flagged in
+// ol.undone for launch_down(..., only = ol.undone).  Shapes: bf16 weights,
+// H % 512 == 0, I % 128 == 0 (expert_mlp_fits).
+bool expert_mlp_fits(int wkind, int H, int I);
+hipError_t launch_expert_mlp(int wkind, bool packed, const void* x, const void* w13,
+                             const void* w2, const int32_t* seg_off, const int32_t* seg_cnt,
+                             const int32_t* sorted_ids, const int32_t* item_seg,
+                             const int32_t* item_row0, const int32_t* n_items, int max_items,
+                             void* h, void* y, int H, int I, int k, OneLaunch ol,
+                             hipStream_t s);
 // Expert weights (bf16 / fp8, a [rows, K] row-major matrix, rows % 16 == 0,
 // K % 32 == 0) -> MFMA fragment order: block (16-row tile t, 32-wide K step
 // s) of 512 elements at (t K/32 + s) 512, lane 16 g + m holding row 16 t + m,

@@ -215,6 +215,24 @@ int moe_forward_signaled(const moe_desc* desc, const void* x, const uint8_t* val
  * MOE_ERR_INVALID_ARG outside the range. */
 int moe_set_signal_wait_us(int32_t us);
 
+/* Calls of moe_forward / moe_forward_noalloc where every expert segment
+ * streams its weights (decode-sized batches): run the gate/up GEMM with
+ * SiLU*mul and the down GEMM in one launch (1) or in two (0, the default)
+ * ("Step3 Inference Optimization on AMD Instinct MI308X", optimisation list:
+ * the MoE one-stage kernel).  In the one launch, blocks take the gate/up
+ * units first and the down units after them from one counter; each gate/up
+ * unit releases its h columns at agent scope and counts itself in its work
+ * item, and each down unit waits for its item's count (bounded in time by
+ * moe_set_signal_wait_us; a unit whose wait runs out is run by a rest pass
+ * after the launch), so the output bits equal the two-launch path's with the
+ * y rows in memory, i.e. except for calls of at most 1216 assignments, which
+ * the default path combines on chip.  Applies to bf16 activations and
+ * weights, H a multiple of 512 and I of 128; other calls, and
+ * moe_forward_signaled, keep two launches.  Host, process-wide, read when a
+ * call is planned (size workspaces after choosing).  MOE_ERR_INVALID_ARG
+ * unless 0 or 1. */
+int moe_set_one_launch(int32_t enable);
+
 /* Bytes of the fixed device scratch that moe_forward_noalloc works in. */
 #define MOE_SCRATCH_BYTES (64u << 20)
 

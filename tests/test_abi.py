@@ -177,7 +177,7 @@ def test_workspace_grows_with_batch():
 def test_profile_hooks_without_records():
     assert moe.stage_names() == ["route_logits", "route_topk", "align", "pack_x", "gate_up",
                                  "gate_up_gemm", "down", "down_gemm", "combine", "x_split",
-                                 "combine_wait"]
+                                 "combine_wait", "expert_mlp"]
     rec = moe.moe_profile_read()
     assert all(v == (0.0, 0) for v in rec.values())
 
@@ -230,6 +230,19 @@ def test_signal_wait_bound_validation():
     assert lib.moe_set_signal_wait_us(1000001) == -1
     assert lib.moe_set_signal_wait_us(0) == 0
     assert lib.moe_set_signal_wait_us(10000) == 0
+
+
+def test_one_launch_switch_validation():
+    lib = moe.load_library()
+    assert lib.moe_set_one_launch(2) == -1 and lib.moe_set_one_launch(-1) == -1
+    d = _d()
+    base = lib.moe_workspace_size(ctypes.byref(d), 3)
+    assert lib.moe_set_one_launch(1) == 0
+    try:
+        # the counters' room is always in the workspace
+        assert lib.moe_workspace_size(ctypes.byref(d), 3) == base
+    finally:
+        assert lib.moe_set_one_launch(0) == 0
 
 
 def test_scratch_bytes_matches_header():
