@@ -148,3 +148,44 @@ def test_one_launch_replays_in_a_hip_graph():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {i}"
         assert torch.isfinite(junk)
+
+
+def _random_shape(seed):
+    """A seeded shape the one launch takes (bf16, H % 512 == 0, I % 128 == 0)."""
+    r = np.random.default_rng(2000 + seed)
+    E = int(r.choice([1, 3, 8, 13, 48, 64, 200]))
+    return dict(T=int(r.choice([1, 5, 33, 100, 257, 700, 1500])), H=int(r.choice([512, 1024, 1536])),
+                E=E, k=int(r.integers(1, min(8, E) + 1)), I=int(r.choice([128, 256, 384])),
+                n_shared=int(r.integers(2)), valid_frac=float(r.choice([1.0, 0.75, 0.3])))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_one_launch_random_shapes(seed):
+    """Seeded random shapes: the oracle's values, the same bits on a second
+    call, and the signaled call's bits (y through memory on both)."""
+    kw = _random_shape(seed)
+    inp = random_small(seed=190 + seed, **kw)
+    log(f"[case] one launch random seed={seed}: {kw}")
+    layer = device_layer(inp, packed=bool(seed % 2))
+    xd = inp.x.cuda()
+    vd = None if inp.valid is None else inp.valid.cuda()
+    sig_out, _ = layer.forward_signaled(xd, vd)
+    with one_launch():
+        gpu = run_gpu(inp, layer)
+        again = layer.forward(xd, vd)
+    torch.cuda.synchronize()
+    assert np.array_equal(gpu["out"], again.float().cpu().double().numpy())
+    compare(inp, gpu)
+    if not _may_tile(kw):
+        # every segment streams in both calls: the same units, the same bits
+        assert torch.equal(again, sig_out)
+
+
+def _may_tile(kw):
+    """Whether the tiled GEMM may take segments of this call (the library's
+    rule: some segment above 128 rows, and enough 128-row tiles to fill the
+    chip at I / 128 blocks each)."""
+    T, kk, I = kw["T"], kw["k"] + kw["n_shared"], kw["I"]
+    min_tiles = (256 + I // 128 - 1) // (I // 128)
+    bound = T * kk // 128 + T * kk // 129 + 1
+    return T > 128 and bound >= min_tiles
