@@ -506,9 +506,10 @@ __global__ __launch_bounds__(256) void down_stream_kernel(
 // calls where every segment streams, bf16 weights.  A block takes tickets
 // from one counter until they run out: the first n_items * n_cg tickets are
 // gate/up units, the next n_items * n_ng down units (the units of the two
-// streaming kernels, run by the same code).  A gate/up unit stores its h columns, releases them
-// at agent scope and counts itself in its item's counter; a down unit waits
-// until its item's counter reaches n_cg, acquires, and runs.  Tickets are
+// streaming kernels, run by the same code).  A gate/up unit stores its h
+// columns, releases them at agent scope and counts itself in its item's
+// counter; a down unit waits until its item's counter reaches n_cg,
+// acquires, and runs.  Tickets are
 // handed out in order to blocks that are running, so every gate/up unit a
 // down unit waits for is held by a running block that waits for nothing: the
 // waits end.  They are also bounded in time (the real-time counter); a wait
@@ -546,8 +547,8 @@ void expert_mlp_kernel(
   for (int tk = next_ticket(); tk < n_all; tk = next_ticket()) {
     if (tk < n_gu) {
       const int item = gate_up_unit<KS, MT, KUG, CGN, false, PW, true>(
-          tk, x, w13, nullptr, seg_off, seg_cnt, item_seg, item_row0, h, H, I, n_cg, sorted_ids, topk,
-          red);
+          tk, x, w13, nullptr, seg_off, seg_cnt, item_seg, item_row0, h, H, I, n_cg, sorted_ids,
+          topk, red);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
