@@ -189,3 +189,24 @@ def _may_tile(kw):
     min_tiles = (256 + I // 128 - 1) // (I // 128)
     bound = T * kk // 128 + T * kk // 129 + 1
     return T > 128 and bound >= min_tiles
+
+
+def test_one_launch_in_the_fixed_scratch():
+    """moe_forward_noalloc takes the one launch too (its counters live in the
+    scratch like every other workspace part): the bits of moe_forward under
+    the same switch, on two calls in a row, the second smaller."""
+    import expert_layer_moe_amd as moe
+    inp = random_small(seed=199, T=300, H=512, E=16, k=3, I=128, n_shared=1, valid_frac=0.8)
+    log("[case] one launch in the fixed scratch")
+    layer = device_layer(inp, packed=True)
+    xd = inp.x.cuda()
+    vd = inp.valid.cuda()
+    with one_launch():
+        for rows in (300, 97):
+            x, v = xd[:rows].contiguous(), vd[:rows].contiguous()
+            ref = layer.forward(x, v)
+            got = torch.full_like(x, float("nan"))
+            moe.moe_forward_noalloc(layer.desc(rows), x, v, layer.router, layer.w13, layer.w2,
+                                    layer.topk, got)
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), rows
