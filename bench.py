@@ -15,7 +15,9 @@ the unsplit 16384-row batch and the request-boundary split (7003 / 9381),
 the tiny fp32 correctness layer, the gather and the prefill micro-batch
 through moe_forward_signaled (per-(expert, 64-row block) completion counters
 from the down kernels, the combine consuming them on a second stream), and
-the two decode workloads with the gate/up and the down in one launch.
+the two decode workloads with the gate/up and the down in one launch, and the
+prefill micro-batch with its gate/up GEMM on the fp8 MFMA (token rows as two
+e4m3 terms, moe_set_fp8_mfma).
 Prints one JSON line.
 
 Other modes (profiling runs; the default run takes none of them):
@@ -23,13 +25,15 @@ Other modes (profiling runs; the default run takes none of them):
                       gather_padded_e48, prefill_ub_fp8, prefill_pair_fp8,
                       prefill_unsplit, prefill_boundary_split,
                       gather_padded_e48_signaled, prefill_ub_fp8_signaled,
-                      decode_e48_one_launch, decode_e256_shared_one_launch)
+                      decode_e48_one_launch, decode_e256_shared_one_launch,
+                      prefill_ub_fp8_fp8_mfma)
   --no-cpu-baseline   skip the oracle timing
   --copy-calibrate    time a plain 1 GiB device copy (for counter scaling)
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import re
 import json
@@ -44,6 +48,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s per MI355X + % of HBM-BW (decode) / MFMA peak (prefill)"
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 CSRC = os.path.join(ROOT, "expert_layer_moe_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -52,13 +57,19 @@ HEADLINE = "decode_e48"
 NESTED = ["decode_e256_shared", "gather_padded_e48", "prefill_ub_fp8", "prefill_pair_fp8",
           "prefill_unsplit", "prefill_boundary_split", "tiny",
           "gather_padded_e48_signaled", "prefill_ub_fp8_signaled",
-          "decode_e48_one_launch", "decode_e256_shared_one_launch"]
+          "decode_e48_one_launch", "decode_e256_shared_one_launch", "prefill_ub_fp8_fp8_mfma"]
 # workloads run through moe_forward_signaled: the down kernels raise
 # per-(expert, 64-row block) completion counters and the combine consumes
 # them on a second stream
 SIGNALED = "_signaled"
 # workloads run with the gate/up and down in one launch (moe_set_one_launch)
 ONE_LAUNCH = "_one_launch"
+# fp8-weight workloads whose gate/up GEMM runs on the fp8 MFMA with the token
+# rows as two e4m3 terms (moe_set_fp8_mfma)
+FP8_MFMA = "_fp8_mfma"
+# the fp8-MFMA switch as the command line sets it for the whole run (a
+# workload that turns it on for its own calls turns it back to this)
+RUN_FP8_MFMA = [False]
 # two-call variants of the prefill workload: (first rows, second rows)
 PREFILL_SPLITS = {"prefill_pair_fp8": "midpoint", "prefill_boundary_split": "boundary"}
 
@@ -88,11 +99,14 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def compute_dtype(cfg) -> str:
+def compute_dtype(cfg, fp8_mfma=False) -> str:
     """The arithmetic type of the expert GEMMs: fp32 FMA for fp32 layers,
     bf16 MFMA (fp32 accumulation) otherwise; fp8 weights are converted to
-    bf16 on the way in."""
-    return "f32" if cfg.act == "f32" else "bf16"
+    bf16 on the way in, except with fp8_mfma, where the gate/up GEMM runs on
+    the fp8 MFMA (two e4m3 token terms) and the rest in bf16."""
+    if cfg.act == "f32":
+        return "f32"
+    return "fp8+bf16" if fp8_mfma and cfg.w == "fp8" else "bf16"
 
 
 def algorithmic_work(cfg, ids, n_valid):
@@ -220,12 +234,16 @@ class Workload:
         self.name = name
         self.signaled = name.endswith(SIGNALED)
         self.one_launch = name.endswith(ONE_LAUNCH)
+        self.fp8_mfma = name.endswith(FP8_MFMA)
         bname = name[:-len(SIGNALED)] if self.signaled else name
         bname = bname[:-len(ONE_LAUNCH)] if self.one_launch else bname
+        bname = bname[:-len(FP8_MFMA)] if self.fp8_mfma else bname
         self.split = PREFILL_SPLITS.get(bname)
         whole = bname in ("prefill_unsplit",) or self.split is not None
         base = get_config("prefill_ub_fp8" if whole else bname)
         self.cfg = base.with_(T=base.full_T, ub=None) if whole else base
+        if self.fp8_mfma and self.cfg.w != "fp8":
+            raise ValueError(f"{name}: the fp8 MFMA path needs fp8 weights")
         log(f"[bench] generating {name}")
         self.inp = make_inputs(self.cfg)
         self.packed = self.cfg.w != "f32" and not row_major
@@ -238,7 +256,10 @@ class Workload:
         self.n_valid = self.inp.n_valid
         if self.split is None:
             self.parts = None
-            self.ws = self.layer.workspace(c.T)
+            # the switch is read when the plan is made: a workspace sized with
+            # it on holds the two-term token planes
+            with self._switches():
+                self.ws = self.layer.workspace(c.T)
             if self.signaled:
                 self.sig = self.layer.block_signals(c.T)
                 self.consumer = torch.cuda.Stream()
@@ -255,21 +276,32 @@ class Workload:
         torch.cuda.synchronize()
         self.work = algorithmic_work(c, ids.cpu().numpy(), self.n_valid)
 
+    @contextlib.contextmanager
+    def _switches(self):
+        """The library's process-wide path switches this workload runs with,
+        on for the duration of one call and off again after it."""
+        import expert_layer_moe_amd as moe
+        if self.one_launch:
+            moe.moe_set_one_launch(True)
+        if self.fp8_mfma:
+            moe.moe_set_fp8_mfma(True)
+        try:
+            yield
+        finally:
+            if self.one_launch:
+                moe.moe_set_one_launch(False)
+            if self.fp8_mfma:
+                moe.moe_set_fp8_mfma(RUN_FP8_MFMA[0])
+
     def step(self):
         import torch
         if self.parts is None:
             if self.signaled:
                 self.layer.forward_signaled(self.x, self.valid, self.out, self.ws, self.sig,
                                             consumer_stream=self.consumer)
-            elif self.one_launch:
-                import expert_layer_moe_amd as moe
-                moe.moe_set_one_launch(True)
-                try:
-                    self.layer.forward(self.x, self.valid, self.out, self.ws)
-                finally:
-                    moe.moe_set_one_launch(False)
             else:
-                self.layer.forward(self.x, self.valid, self.out, self.ws)
+                with self._switches():
+                    self.layer.forward(self.x, self.valid, self.out, self.ws)
             return
         cur = torch.cuda.current_stream()
         ev = torch.cuda.Event()
@@ -307,9 +339,12 @@ def roofline(wl, dom, avg_s):
     w = wl.work
     ai = w["gate_up_flops"] / w["gate_up_bytes"]
     if ai > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        # a GEMM on the fp8 MFMA is priced against the fp8 peak (its
+        # algorithmic flops, not the two terms' issued ones)
+        peak = PEAK_FP8_TFLOPS if wl.fp8_mfma else PEAK_BF16_TFLOPS
         ach = w["gate_up_flops"] / avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4)}
     else:
         ach = w["gate_up_bytes"] / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
@@ -342,6 +377,8 @@ def config_of(wl):
         cfg["block_signals"] = True
     if wl.one_launch:
         cfg["one_launch_gate_up_down"] = True
+    if c.w == "fp8":
+        cfg["fp8_gate_up_gemm"] = "fp8_mfma_two_term" if wl.fp8_mfma else "bf16_mfma"
     if wl.parts is not None:
         cfg["calls_rows"] = list(wl.rows)
     return cfg
@@ -370,7 +407,7 @@ def measure_nested(name, steps, warmup):
         wl.step()
     ms = time_steps(wl.step, steps)
     rec = {"ms_per_step": round(ms, 5), "tokens_per_s": round(wl.n_valid / (ms / 1e3), 1),
-           "steps": steps, "warmup": warmup, "dtype": compute_dtype(wl.cfg),
+           "steps": steps, "warmup": warmup, "dtype": compute_dtype(wl.cfg, wl.fp8_mfma),
            "config": config_of(wl)}
     rec["step"] = step_fractions(wl, ms)
     if wl.one_launch:
@@ -429,13 +466,14 @@ def run_headline(args, name):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None,
-        "dtype": compute_dtype(wl.cfg), "data": "synthetic",
+        "dtype": compute_dtype(wl.cfg, wl.fp8_mfma or args.fp8_mfma), "data": "synthetic",
         "config": config_of(wl),
     }
     if args.gemm_min_rows is not None:
         res["config"]["gemm_thresholds"] = [args.gemm_min_rows, args.gemm_min_tiles]
     if wl.cfg.w == "fp8":
-        res["config"]["fp8_gate_up_gemm"] = "fp8_mfma_two_term" if args.fp8_mfma else "bf16_mfma"
+        res["config"]["fp8_gate_up_gemm"] = ("fp8_mfma_two_term" if args.fp8_mfma or wl.fp8_mfma
+                                             else "bf16_mfma")
     if dom:
         g_ms, g_n = dom_rec[dom]
         roof = roofline(wl, dom, g_ms / max(g_n, 1) / 1e3)
@@ -476,6 +514,7 @@ def run(args):
     if args.gemm_min_rows is not None:
         moe.moe_set_path_thresholds(args.gemm_min_rows, args.gemm_min_tiles)
     if args.fp8_mfma:
+        RUN_FP8_MFMA[0] = True
         moe.moe_set_fp8_mfma(True)
     if args.copy_calibrate:
         n = 1 << 30

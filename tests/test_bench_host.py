@@ -42,6 +42,24 @@ def test_dtype_follows_the_workload():
     assert bench.compute_dtype(get_config("decode_e48")) == "bf16"
     # fp8 weights are converted to bf16 for bf16 MFMA
     assert bench.compute_dtype(get_config("prefill_ub_fp8")) == "bf16"
+    # ... unless the gate/up GEMM runs on the fp8 MFMA
+    assert bench.compute_dtype(get_config("prefill_ub_fp8"), fp8_mfma=True) == "fp8+bf16"
+    assert bench.compute_dtype(get_config("decode_e48"), fp8_mfma=True) == "bf16"
+
+
+def test_nested_workload_names_resolve():
+    """Every nested workload name strips to a configured base workload, and
+    the fp8-MFMA variants are fp8-weight layers."""
+    from workloads import get_config
+    for name in bench.NESTED:
+        base = name
+        for suffix in (bench.SIGNALED, bench.ONE_LAUNCH, bench.FP8_MFMA):
+            if base.endswith(suffix):
+                base = base[:-len(suffix)]
+        base = "prefill_ub_fp8" if base in bench.PREFILL_SPLITS or base == "prefill_unsplit" else base
+        cfg = get_config(base)
+        if name.endswith(bench.FP8_MFMA):
+            assert cfg.w == "fp8"
 
 
 def test_host_info_names_the_cpu():
